@@ -1,0 +1,97 @@
+"""A paged KV cache over the C ABI: slabs for owning layers only.
+
+Every layer that owns KV gets its own K/V slab (and scales for the int8
+per-token-head format); a KV-shared layer gets none and reads its source's slab
+through the library's layer map (unsloth commit dee9371, "scripts": shared
+layers reference the store layer's cache; FreeToken PR #898, description: the
+pool allocates slabs only for layers that own KV).  PyTorch provides the device
+memory and the stream; all computation is in libpakv.so.
+"""
+
+import torch
+
+from . import pakv
+
+SLIDING, FULL = 0, 1
+
+
+class PagedKVCache:
+    """layers: sequence of objects or dicts with head_dim, num_q_heads,
+    num_kv_heads, window (0 = full), kv_dtype ("bf16" / "int8") and sm_scale.
+    first_shared: index of the first KV-shared layer, or None."""
+
+    def __init__(self, layers, first_shared, num_pages, device="cuda", sentinel=True):
+        get = (lambda l, k: l[k]) if isinstance(layers[0], dict) else (lambda l, k: getattr(l, k))
+        self.specs = [{k: get(l, k) for k in ("head_dim", "num_q_heads", "num_kv_heads", "window",
+                                              "kv_dtype", "sm_scale")} for l in layers]
+        n = len(self.specs)
+        types = [SLIDING if s["window"] > 0 else FULL for s in self.specs]
+        fs = n if first_shared is None else first_shared
+        self.sources = pakv.resolve_kv_sources(types, fs)
+        descs = []
+        for l, s in enumerate(self.specs):
+            descs.append(pakv.LayerDesc(s["head_dim"], s["num_q_heads"], s["num_kv_heads"], s["window"],
+                                        -1 if self.sources[l] == l else self.sources[l],
+                                        pakv.KV_BF16 if s["kv_dtype"] == "bf16" else pakv.KV_INT8_PTH,
+                                        float(s["sm_scale"])))
+        self.map = pakv.LayerMap(descs)
+        self.num_pages = num_pages
+        self.device = torch.device(device)
+        self.slabs = {}
+        for l, s in enumerate(self.specs):
+            if self.sources[l] != l:
+                continue
+            hkv, d = s["num_kv_heads"], s["head_dim"]
+            if s["kv_dtype"] == "bf16":
+                fill = 0x7FC0 if sentinel else 0            # bf16 quiet NaN
+                k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int16, device=self.device)
+                v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int16, device=self.device)
+                ks = vs = None
+            else:
+                fill = -128 if sentinel else 0
+                k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int8, device=self.device)
+                v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int8, device=self.device)
+                sfill = float("nan") if sentinel else 0.0
+                ks = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
+                vs = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
+            self.map.bind_slab(l, k, v, num_pages, ks, vs)
+            self.slabs[l] = (k, v, ks, vs)
+        self.pages = None
+        self.page_table = None
+        self._workspace = None
+
+    def slab_of(self, layer):
+        return self.slabs[self.sources[layer]]
+
+    def set_page_table(self, page_table):
+        """page_table: int32 [B, max_pages] (host or device)."""
+        self.page_table = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
+        self.pages = pakv.make_pages(self.page_table)
+
+    def store(self, layer, cu_tokens, start_pos, k, v, stream=None):
+        total = k.shape[0]
+        nseq = cu_tokens.shape[0] - 1
+        pakv.paged_kv_store(self.map, layer, self.pages, cu_tokens, start_pos, k, v, nseq, total, stream)
+
+    def workspace(self, layer, num_seqs, max_kv_len):
+        need = pakv.decode_workspace_bytes(self.map, layer, num_seqs, max_kv_len)
+        if self._workspace is None or self._workspace.numel() < need:
+            self._workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._workspace, need
+
+    def decode(self, layer, kv_lens, q, max_kv_len, out=None, stream=None):
+        nseq = q.shape[0]
+        if out is None:
+            out = torch.empty_like(q)
+        ws, need = self.workspace(layer, nseq, max_kv_len)
+        pakv.paged_attn_decode(self.map, layer, self.pages, kv_lens, q, out, nseq, max_kv_len,
+                               ws, ws.numel(), stream)
+        return out
+
+    def extend(self, layer, cu_q, prefix_lens, q, max_q_len, max_kv_len, out=None, stream=None):
+        nseq = cu_q.shape[0] - 1
+        if out is None:
+            out = torch.empty_like(q)
+        pakv.paged_attn_extend(self.map, layer, self.pages, cu_q, prefix_lens, q, out, nseq, q.shape[0],
+                               max_q_len, max_kv_len, stream)
+        return out

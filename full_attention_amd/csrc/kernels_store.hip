@@ -1,0 +1,178 @@
+// paged_kv_store: scatter new K/V rows into a layer's slab.
+//
+// One wavefront per (token, KV head) row.  bf16 rows are copied bit for bit;
+// int8 per-token-head rows are encoded in-kernel: amax over the row, one IEEE
+// float32 division for the scale, one per element, round half to even, clamp
+// to +-127 (the library's reading of the per-token-head format described in
+// FreeToken PR #898, description bullet on the 8-bit formats).
+//
+// K pages are token-major ([16][D]); V pages are dim-major ([D][16]), so a V
+// row lands as D strided 2-byte (or 1-byte) stores.
+
+#include "device_common.h"
+#include "pakv_internal.h"
+
+using namespace pakv_dev;
+
+namespace {
+
+struct StoreArgs {
+    uint8_t* k_slab;
+    uint8_t* v_slab;
+    float* k_scale;
+    float* v_scale;
+    int32_t num_pages;
+    const int32_t* page_table;
+    int32_t max_pages;
+    const int32_t* cu_tokens;
+    const int32_t* start_pos;
+    const uint16_t* k;
+    const uint16_t* v;
+    int32_t num_seqs;
+    int32_t total_tokens;
+    int32_t hkv;
+};
+
+// Physical row address of (token t, head h), or false if the row falls outside
+// the page table or the pool.
+__device__ __forceinline__ bool locate(const StoreArgs& a, int32_t t, int32_t h,
+                                       int64_t& page_head, int32_t& slot) {
+    // largest b with cu_tokens[b] <= t
+    int32_t lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+        int32_t mid = (lo + hi + 1) >> 1;
+        if (a.cu_tokens[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int32_t b = lo;
+    const int32_t pos = a.start_pos[b] + (t - a.cu_tokens[b]);
+    if (pos < 0) return false;
+    const int32_t pg = pos >> 4;
+    if (pg >= a.max_pages) return false;
+    const int32_t phys = a.page_table[(int64_t)b * a.max_pages + pg];
+    if ((uint32_t)phys >= (uint32_t)a.num_pages) return false;
+    page_head = (int64_t)phys * a.hkv + h;
+    slot = pos & 15;
+    return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
+    constexpr int EPL = D / 64;   // elements per lane: 4 or 8
+    const int32_t lane = threadIdx.x & 63;
+    const int32_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int32_t h = blockIdx.y;
+    if (t >= a.total_tokens) return;
+    int64_t ph;
+    int32_t slot;
+    if (!locate(a, t, h, ph, slot)) return;
+    const int64_t src = ((int64_t)t * a.hkv + h) * D + lane * EPL;
+    uint16_t kv[EPL], vv[EPL];
+    if constexpr (EPL == 8) {
+        *reinterpret_cast<u32x4*>(kv) = *reinterpret_cast<const u32x4*>(a.k + src);
+        *reinterpret_cast<u32x4*>(vv) = *reinterpret_cast<const u32x4*>(a.v + src);
+    } else {
+        *reinterpret_cast<u32x2*>(kv) = *reinterpret_cast<const u32x2*>(a.k + src);
+        *reinterpret_cast<u32x2*>(vv) = *reinterpret_cast<const u32x2*>(a.v + src);
+    }
+    uint16_t* kdst = reinterpret_cast<uint16_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
+    if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(kdst) = *reinterpret_cast<u32x4*>(kv);
+    else *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kv);
+    uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_slab) + ph * kPage * D + slot;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vdst[(lane * EPL + e) * kPage] = vv[e];
+}
+
+// Encodes EPL bf16 values of one lane into int8 codes given the row's scale.
+template <int EPL>
+__device__ __forceinline__ void encode(const float (&x)[EPL], float scale, int8_t (&code)[EPL]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        float c = 0.0f;
+        if (scale > 0.0f) {
+            c = __builtin_rintf(x[e] / scale);
+            c = fminf(fmaxf(c, -127.0f), 127.0f);
+        }
+        code[e] = (int8_t)(int)c;
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void store_int8_kernel(StoreArgs a) {
+    constexpr int EPL = D / 64;
+    const int32_t lane = threadIdx.x & 63;
+    const int32_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int32_t h = blockIdx.y;
+    if (t >= a.total_tokens) return;
+    int64_t ph;
+    int32_t slot;
+    if (!locate(a, t, h, ph, slot)) return;
+    const int64_t src = ((int64_t)t * a.hkv + h) * D + lane * EPL;
+    float kx[EPL], vx[EPL];
+    float kmax = 0.0f, vmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        kx[e] = bf16_bits_to_f32(a.k[src + e]);
+        vx[e] = bf16_bits_to_f32(a.v[src + e]);
+        kmax = fmaxf(kmax, fabsf(kx[e]));
+        vmax = fmaxf(vmax, fabsf(vx[e]));
+    }
+    kmax = wave_max(kmax);
+    vmax = wave_max(vmax);
+    const float ks = kmax / 127.0f;   // IEEE division (no fast-math in this build)
+    const float vs = vmax / 127.0f;
+    int8_t kc[EPL], vc[EPL];
+    encode<EPL>(kx, ks, kc);
+    encode<EPL>(vx, vs, vc);
+    int8_t* kdst = reinterpret_cast<int8_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
+    if constexpr (EPL == 8) *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kc);
+    else *reinterpret_cast<uint32_t*>(kdst) = *reinterpret_cast<uint32_t*>(kc);
+    int8_t* vdst = reinterpret_cast<int8_t*>(a.v_slab) + ph * kPage * D + slot;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vdst[(lane * EPL + e) * kPage] = vc[e];
+    if (lane == 0) {
+        a.k_scale[ph * kPage + slot] = ks;
+        a.v_scale[ph * kPage + slot] = vs;
+    }
+}
+
+}  // namespace
+
+namespace pakv {
+
+int launch_store(const StoreLaunch& s, void* stream) {
+    StoreArgs a;
+    a.k_slab = static_cast<uint8_t*>(const_cast<void*>(s.slab.k));
+    a.v_slab = static_cast<uint8_t*>(const_cast<void*>(s.slab.v));
+    a.k_scale = const_cast<float*>(s.slab.k_scale);
+    a.v_scale = const_cast<float*>(s.slab.v_scale);
+    a.num_pages = s.slab.num_pages;
+    a.page_table = s.page_table;
+    a.max_pages = s.max_pages;
+    a.cu_tokens = s.cu_tokens;
+    a.start_pos = s.start_pos;
+    a.k = s.k;
+    a.v = s.v;
+    a.num_seqs = s.num_seqs;
+    a.total_tokens = s.total_tokens;
+    a.hkv = s.hkv;
+    dim3 grid((s.total_tokens + 3) / 4, s.hkv);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.kv_dtype == PAKV_KV_BF16) {
+        if (s.head_dim == 256) hipLaunchKernelGGL(store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
+    } else {
+        if (s.head_dim == 256) hipLaunchKernelGGL(store_int8_kernel<256>, grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(store_int8_kernel<512>, grid, dim3(256), 0, st, a);
+    }
+    return (int)hipGetLastError();
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace pakv

@@ -1,0 +1,346 @@
+// C ABI of the paged KV-cache attention library: argument checks, the layer
+// map (ownership and KV-source aliasing), the decode split plan and dispatch to
+// the kernel launchers.  Nothing here touches the GPU before every argument has
+// been checked.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "pakv_internal.h"
+
+namespace pakv {
+
+static thread_local std::string g_last_error;
+
+pakv_status fail(pakv_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+// Tokens per split.  Longer contexts take longer splits so that the partial
+// results stay a few percent of the KV bytes; every split is a whole number of
+// 64-token steps (4 waves x one 16-token page each).
+DecodePlan plan_decode(const pakv_layer_desc& d, int32_t max_kv_len) {
+    DecodePlan p{};
+    int64_t span = max_kv_len;
+    if (d.window > 0 && d.window < span) span = d.window;
+    int32_t s = 128;
+    if (span > 2048) s = 256;
+    if (span > 8192) s = 512;
+    if (span > 32768) s = 1024;
+    p.split_tokens = s;
+    // Splits are aligned to multiples of S in absolute positions, so a window
+    // of W positions can touch ceil((W + S - 1) / S) of them.
+    int64_t reach = (d.window > 0) ? (int64_t)d.window + s - 1 : (int64_t)max_kv_len;
+    if (reach > max_kv_len) reach = max_kv_len;
+    int64_t n = (reach + s - 1) / s;
+    if (d.window > 0) {
+        int64_t full_n = ((int64_t)max_kv_len + s - 1) / s;
+        if (n > full_n) n = full_n;
+    }
+    p.max_splits = (int32_t)(n < 1 ? 1 : n);
+    p.group = d.num_q_heads / d.num_kv_heads;
+    return p;
+}
+
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len) {
+    DecodePlan p = plan_decode(d, max_kv_len);
+    size_t units = (size_t)num_seqs * d.num_kv_heads * p.max_splits * p.group;
+    size_t o = units * d.head_dim * sizeof(float);
+    o = (o + 255) & ~(size_t)255;
+    return o + units * 2 * sizeof(float);
+}
+
+static bool layer_ok(const pakv_layer_map* m, int32_t layer) {
+    return m && layer >= 0 && layer < (int32_t)m->layers.size();
+}
+
+}  // namespace pakv
+
+using namespace pakv;
+
+extern "C" {
+
+const char* pakv_last_error(void) { return g_last_error.c_str(); }
+
+pakv_status pakv_resolve_kv_sources(int32_t n_layers, const int32_t* layer_type,
+                                    int32_t first_shared, int32_t* out_source) {
+    clear_error();
+    if (n_layers < 0) return fail(PAKV_ERR_INVALID, "n_layers < 0");
+    if (n_layers > 0 && (!layer_type || !out_source)) return fail(PAKV_ERR_INVALID, "null pointer");
+    if (first_shared < 0) return fail(PAKV_ERR_INVALID, "first_shared < 0");
+    std::vector<int32_t> src(n_layers);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (l < first_shared) { src[l] = l; continue; }
+        int32_t found = -1;
+        for (int32_t i = first_shared - 1; i >= 0; --i) {
+            if (i < n_layers && layer_type[i] == layer_type[l]) { found = i; break; }
+        }
+        if (found < 0)
+            return fail(PAKV_ERR_ALIAS, "KV-shared layer %d has no earlier layer of its type (%d)",
+                        l, layer_type[l]);
+        src[l] = found;
+    }
+    for (int32_t l = 0; l < n_layers; ++l) out_source[l] = src[l];
+    return PAKV_OK;
+}
+
+pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_layer_map** out) {
+    clear_error();
+    if (!out) return fail(PAKV_ERR_INVALID, "out is null");
+    *out = nullptr;
+    if (n <= 0) return fail(PAKV_ERR_INVALID, "a layer map needs at least one layer");
+    if (!descs) return fail(PAKV_ERR_INVALID, "descs is null");
+    for (int32_t l = 0; l < n; ++l) {
+        const pakv_layer_desc& d = descs[l];
+        if (d.head_dim != 256 && d.head_dim != 512)
+            return fail(PAKV_ERR_UNSUPPORTED, "layer %d: head_dim %d (256 or 512 supported)", l, d.head_dim);
+        if (d.num_kv_heads < 1 || d.num_q_heads < 1)
+            return fail(PAKV_ERR_INVALID, "layer %d: head counts must be positive", l);
+        if (d.num_q_heads % d.num_kv_heads != 0)
+            return fail(PAKV_ERR_INVALID, "layer %d: Hq %d is not a multiple of Hkv %d", l,
+                        d.num_q_heads, d.num_kv_heads);
+        if (d.num_q_heads / d.num_kv_heads > 16)
+            return fail(PAKV_ERR_UNSUPPORTED, "layer %d: group size %d above 16", l,
+                        d.num_q_heads / d.num_kv_heads);
+        if (d.window < 0) return fail(PAKV_ERR_INVALID, "layer %d: negative window", l);
+        if (d.kv_dtype != PAKV_KV_BF16 && d.kv_dtype != PAKV_KV_INT8_PTH)
+            return fail(PAKV_ERR_INVALID, "layer %d: unknown kv_dtype %d", l, d.kv_dtype);
+        if (!(d.sm_scale > 0.0f) || d.sm_scale != d.sm_scale || d.sm_scale > 1e30f)
+            return fail(PAKV_ERR_INVALID, "layer %d: sm_scale must be positive and finite", l);
+        if (d.kv_source != -1) {
+            int32_t s = d.kv_source;
+            if (s < 0 || s >= l)
+                return fail(PAKV_ERR_ALIAS, "layer %d: kv_source %d is not an earlier layer", l, s);
+            const pakv_layer_desc& sd = descs[s];
+            if (sd.kv_source != -1)
+                return fail(PAKV_ERR_ALIAS, "layer %d: kv_source %d is itself KV-shared", l, s);
+            if (sd.head_dim != d.head_dim || sd.num_kv_heads != d.num_kv_heads ||
+                sd.window != d.window || sd.kv_dtype != d.kv_dtype)
+                return fail(PAKV_ERR_ALIAS,
+                            "layer %d: kv_source %d differs in head_dim, num_kv_heads, window or kv_dtype",
+                            l, s);
+        }
+    }
+    pakv_layer_map* m = new (std::nothrow) pakv_layer_map;
+    if (!m) return fail(PAKV_ERR_INVALID, "out of host memory");
+    m->layers.resize(n);
+    for (int32_t l = 0; l < n; ++l) {
+        m->layers[l].desc = descs[l];
+        m->layers[l].source = descs[l].kv_source == -1 ? l : descs[l].kv_source;
+        m->layers[l].bound = false;
+        std::memset(&m->layers[l].slab, 0, sizeof(pakv_slab));
+    }
+    *out = m;
+    return PAKV_OK;
+}
+
+void pakv_layer_map_destroy(pakv_layer_map* map) { delete map; }
+
+pakv_status pakv_layer_map_bind_slab(pakv_layer_map* map, int32_t layer, const pakv_slab* slab) {
+    clear_error();
+    if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
+    if (!slab) return fail(PAKV_ERR_INVALID, "slab is null");
+    auto& L = map->layers[layer];
+    if (L.source != layer)
+        return fail(PAKV_ERR_ALIAS, "layer %d is KV-shared (reads layer %d) and owns no slab", layer, L.source);
+    if (slab->page_size != PAKV_PAGE_SIZE)
+        return fail(PAKV_ERR_UNSUPPORTED, "page_size %d (16 supported)", slab->page_size);
+    if (slab->num_pages <= 0) return fail(PAKV_ERR_INVALID, "num_pages must be positive");
+    if (!slab->k || !slab->v) return fail(PAKV_ERR_INVALID, "slab k or v is null");
+    if (L.desc.kv_dtype == PAKV_KV_INT8_PTH && (!slab->k_scale || !slab->v_scale))
+        return fail(PAKV_ERR_INVALID, "int8 slab needs k_scale and v_scale");
+    L.slab = *slab;
+    L.bound = true;
+    return PAKV_OK;
+}
+
+pakv_status pakv_layer_map_source(const pakv_layer_map* map, int32_t layer, int32_t* src) {
+    clear_error();
+    if (!layer_ok(map, layer) || !src) return fail(PAKV_ERR_INVALID, "bad map, layer or src");
+    *src = map->layers[layer].source;
+    return PAKV_OK;
+}
+
+pakv_status pakv_kv_bytes_per_token(const pakv_layer_map* map, int64_t* full_bytes, int64_t* window_bytes) {
+    clear_error();
+    if (!map || !full_bytes || !window_bytes) return fail(PAKV_ERR_INVALID, "null pointer");
+    int64_t f = 0, w = 0;
+    for (size_t l = 0; l < map->layers.size(); ++l) {
+        const auto& L = map->layers[l];
+        if (L.source != (int32_t)l) continue;
+        const pakv_layer_desc& d = L.desc;
+        int64_t row = d.kv_dtype == PAKV_KV_BF16 ? 2 * (int64_t)d.head_dim : (int64_t)d.head_dim + 4;
+        int64_t bytes = (int64_t)d.num_kv_heads * 2 * row;
+        if (d.window == 0) f += bytes; else w += bytes;
+    }
+    *full_bytes = f;
+    *window_bytes = w;
+    return PAKV_OK;
+}
+
+pakv_status pakv_slab_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_pages,
+                            size_t* code_bytes, size_t* scale_bytes) {
+    clear_error();
+    if (!layer_ok(map, layer) || !code_bytes || !scale_bytes) return fail(PAKV_ERR_INVALID, "bad arguments");
+    if (num_pages < 0) return fail(PAKV_ERR_INVALID, "num_pages < 0");
+    const pakv_layer_desc& d = map->layers[layer].desc;
+    size_t rows = (size_t)num_pages * d.num_kv_heads * PAKV_PAGE_SIZE;
+    *code_bytes = rows * d.head_dim * (d.kv_dtype == PAKV_KV_BF16 ? 2 : 1);
+    *scale_bytes = d.kv_dtype == PAKV_KV_BF16 ? 0 : rows * sizeof(float);
+    return PAKV_OK;
+}
+
+static pakv_status check_pages(const pakv_pages* pages, int32_t num_seqs) {
+    if (!pages || !pages->page_table) return fail(PAKV_ERR_INVALID, "pages or page_table is null");
+    if (pages->max_pages_per_seq <= 0) return fail(PAKV_ERR_INVALID, "max_pages_per_seq must be positive");
+    if (pages->num_seqs < num_seqs)
+        return fail(PAKV_ERR_INVALID, "page table has %d sequences, call needs %d", pages->num_seqs, num_seqs);
+    return PAKV_OK;
+}
+
+static SlabView view_of(const pakv_layer_map::Layer& src) {
+    SlabView s;
+    s.k = src.slab.k;
+    s.v = src.slab.v;
+    s.k_scale = src.slab.k_scale;
+    s.v_scale = src.slab.v_scale;
+    s.num_pages = src.slab.num_pages;
+    return s;
+}
+
+static pakv_status hip_status(int err, const char* what) {
+    if (err == 0) return PAKV_OK;
+    return fail(PAKV_ERR_HIP, "%s: %s", what, hip_error_string(err));
+}
+
+pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                const int32_t* cu_tokens, const int32_t* start_pos,
+                                const void* k, const void* v,
+                                int32_t num_seqs, int32_t total_tokens, void* stream) {
+    clear_error();
+    if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
+    const auto& L = map->layers[layer];
+    if (L.source != layer) return PAKV_OK;   // shared layer: the source already stored these rows
+    if (num_seqs < 0 || total_tokens < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
+    if (pakv_status s = check_pages(pages, num_seqs)) return s;
+    if (!cu_tokens || !start_pos) return fail(PAKV_ERR_INVALID, "cu_tokens or start_pos is null");
+    if (total_tokens > 0 && (!k || !v)) return fail(PAKV_ERR_INVALID, "k or v is null");
+    if (!L.bound) return fail(PAKV_ERR_INVALID, "layer %d has no slab bound", layer);
+    if (total_tokens == 0 || num_seqs == 0) return PAKV_OK;
+    StoreLaunch a;
+    a.slab = view_of(L);
+    a.page_table = pages->page_table;
+    a.max_pages = pages->max_pages_per_seq;
+    a.cu_tokens = cu_tokens;
+    a.start_pos = start_pos;
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.num_seqs = num_seqs;
+    a.total_tokens = total_tokens;
+    a.hkv = L.desc.num_kv_heads;
+    a.head_dim = L.desc.head_dim;
+    a.kv_dtype = L.desc.kv_dtype;
+    return hip_status(launch_store(a, stream), "paged_kv_store launch");
+}
+
+size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
+                                   int32_t num_seqs, int32_t max_kv_len) {
+    if (!layer_ok(map, layer) || num_seqs < 0 || max_kv_len < 1) return 0;
+    return decode_workspace_bytes(map->layers[layer].desc, num_seqs, max_kv_len);
+}
+
+pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* kv_lens, const void* q, void* out,
+                                   int32_t num_seqs, int32_t max_kv_len,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
+    if (num_seqs < 0) return fail(PAKV_ERR_INVALID, "num_seqs < 0");
+    if (num_seqs == 0) return PAKV_OK;
+    if (max_kv_len < 1) return fail(PAKV_ERR_INVALID, "max_kv_len must be at least 1");
+    if (pakv_status s = check_pages(pages, num_seqs)) return s;
+    if ((int64_t)max_kv_len > (int64_t)pages->max_pages_per_seq * PAKV_PAGE_SIZE)
+        return fail(PAKV_ERR_INVALID, "max_kv_len %d exceeds the page table's %d positions", max_kv_len,
+                    pages->max_pages_per_seq * PAKV_PAGE_SIZE);
+    if (!kv_lens || !q || !out) return fail(PAKV_ERR_INVALID, "kv_lens, q or out is null");
+    const auto& L = map->layers[layer];
+    const auto& S = map->layers[L.source];
+    if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
+    size_t need = decode_workspace_bytes(L.desc, num_seqs, max_kv_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    DecodeLaunch a;
+    a.slab = view_of(S);
+    a.page_table = pages->page_table;
+    a.max_pages = pages->max_pages_per_seq;
+    a.kv_lens = kv_lens;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.num_seqs = num_seqs;
+    a.max_kv_len = max_kv_len;
+    a.hq = L.desc.num_q_heads;
+    a.hkv = L.desc.num_kv_heads;
+    a.head_dim = L.desc.head_dim;
+    a.window = L.desc.window;
+    a.kv_dtype = L.desc.kv_dtype;
+    a.sm_scale = L.desc.sm_scale;
+    a.plan = plan_decode(L.desc, max_kv_len);
+    size_t units = (size_t)num_seqs * a.hkv * a.plan.max_splits * a.plan.group;
+    size_t o_bytes = (units * a.head_dim * sizeof(float) + 255) & ~(size_t)255;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
+}
+
+pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* cu_q, const int32_t* prefix_lens,
+                                   const void* q, void* out,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                   int32_t max_kv_len, void* stream) {
+    clear_error();
+    if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
+    if (num_seqs < 0 || total_q < 0 || max_q_len < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
+    if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PAKV_OK;
+    if (pakv_status s = check_pages(pages, num_seqs)) return s;
+    if (max_kv_len < max_q_len) return fail(PAKV_ERR_INVALID, "max_kv_len below max_q_len");
+    if ((int64_t)max_kv_len > (int64_t)pages->max_pages_per_seq * PAKV_PAGE_SIZE)
+        return fail(PAKV_ERR_INVALID, "max_kv_len %d exceeds the page table's %d positions", max_kv_len,
+                    pages->max_pages_per_seq * PAKV_PAGE_SIZE);
+    if (!cu_q || !prefix_lens || !q || !out) return fail(PAKV_ERR_INVALID, "null pointer argument");
+    const auto& L = map->layers[layer];
+    if (L.desc.kv_dtype != PAKV_KV_BF16)
+        return fail(PAKV_ERR_UNSUPPORTED, "extend on an int8 layer is not built");
+    const auto& S = map->layers[L.source];
+    if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
+    ExtendLaunch a;
+    a.slab = view_of(S);
+    a.page_table = pages->page_table;
+    a.max_pages = pages->max_pages_per_seq;
+    a.cu_q = cu_q;
+    a.prefix_lens = prefix_lens;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.max_kv_len = max_kv_len;
+    a.hq = L.desc.num_q_heads;
+    a.hkv = L.desc.num_kv_heads;
+    a.head_dim = L.desc.head_dim;
+    a.window = L.desc.window;
+    a.sm_scale = L.desc.sm_scale;
+    return hip_status(launch_extend(a, stream), "paged_attn_extend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pakv.h"
+
+struct pakv_layer_map {
+    struct Layer {
+        pakv_layer_desc desc;
+        int32_t source;     // layer whose slab this layer reads (itself for an owner)
+        bool bound;         // a slab is attached (owners only)
+        pakv_slab slab;
+    };
+    std::vector<Layer> layers;
+};
+
+namespace pakv {
+
+pakv_status fail(pakv_status code, const char* fmt, ...);
+void clear_error();
+
+// ---- decode split plan: a pure function of (layer desc, max_kv_len) --------
+struct DecodePlan {
+    int32_t split_tokens;   // S: tokens per split (multiple of 64)
+    int32_t max_splits;     // grid extent over splits
+    int32_t group;          // Hq / Hkv
+};
+DecodePlan plan_decode(const pakv_layer_desc& d, int32_t max_kv_len);
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len);
+
+// ---- launchers (defined in the .hip translation units) ----------------------
+struct SlabView {
+    const void* k;
+    const void* v;
+    const float* k_scale;
+    const float* v_scale;
+    int32_t num_pages;
+};
+
+struct StoreLaunch {
+    SlabView slab;          // written through the const-casted pointers
+    const int32_t* page_table;
+    int32_t max_pages;
+    const int32_t* cu_tokens;
+    const int32_t* start_pos;
+    const uint16_t* k;
+    const uint16_t* v;
+    int32_t num_seqs;
+    int32_t total_tokens;
+    int32_t hkv;
+    int32_t head_dim;
+    int32_t kv_dtype;
+};
+int launch_store(const StoreLaunch& a, void* stream);   // returns hipError_t
+
+struct DecodeLaunch {
+    SlabView slab;
+    const int32_t* page_table;
+    int32_t max_pages;
+    const int32_t* kv_lens;
+    const uint16_t* q;
+    uint16_t* out;
+    int32_t num_seqs;
+    int32_t max_kv_len;
+    int32_t hq;
+    int32_t hkv;
+    int32_t head_dim;
+    int32_t window;
+    int32_t kv_dtype;
+    float sm_scale;
+    DecodePlan plan;
+    float* part_o;    // [B][Hkv][max_splits][G][D]
+    float* part_ml;   // [B][Hkv][max_splits][G][2]
+};
+int launch_decode(const DecodeLaunch& a, void* stream);
+
+struct ExtendLaunch {
+    SlabView slab;
+    const int32_t* page_table;
+    int32_t max_pages;
+    const int32_t* cu_q;
+    const int32_t* prefix_lens;
+    const uint16_t* q;
+    uint16_t* out;
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t max_q_len;
+    int32_t max_kv_len;
+    int32_t hq;
+    int32_t hkv;
+    int32_t head_dim;
+    int32_t window;
+    float sm_scale;
+};
+int launch_extend(const ExtendLaunch& a, void* stream);
+
+const char* hip_error_string(int err);
+
+}  // namespace pakv

@@ -1,0 +1,198 @@
+"""ctypes binding of libpakv.so, with the C ABI's names minus the ``pakv_`` prefix.
+
+Argument marshalling only: tensors become device addresses, the current torch
+stream becomes the hipStream_t.  Every computation runs in the library's HIP
+kernels; if the library is missing, importing this module fails.
+"""
+
+import ctypes
+import os
+
+# torch's ROCm build ships its own HIP runtime.  It has to be in the process
+# before libpakv.so is loaded, so that the library's libamdhip64.so.7
+# dependency resolves (by soname) to that same runtime: one HIP runtime per
+# process, and torch's stream handles are valid for the library's launches.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpakv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(or python -m full_attention_amd.build)")
+lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(6)
+KV_BF16, KV_INT8_PTH = 0, 1
+PAGE_SIZE = 16
+
+EXPORTED = (
+    "pakv_last_error", "pakv_resolve_kv_sources", "pakv_layer_map_create", "pakv_layer_map_destroy",
+    "pakv_layer_map_bind_slab", "pakv_layer_map_source", "pakv_kv_bytes_per_token", "pakv_slab_bytes",
+    "pakv_paged_kv_store", "pakv_decode_workspace_bytes", "pakv_paged_attn_decode",
+    "pakv_paged_attn_extend",
+)
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("kv_source", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class Slab(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+class Pages(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+
+lib.pakv_last_error.restype = ctypes.c_char_p
+lib.pakv_last_error.argtypes = []
+lib.pakv_resolve_kv_sources.restype = _I
+lib.pakv_resolve_kv_sources.argtypes = [_I, _P, _I, _P]
+lib.pakv_layer_map_create.restype = _I
+lib.pakv_layer_map_create.argtypes = [_P, _I, ctypes.POINTER(_P)]
+lib.pakv_layer_map_destroy.restype = None
+lib.pakv_layer_map_destroy.argtypes = [_P]
+lib.pakv_layer_map_bind_slab.restype = _I
+lib.pakv_layer_map_bind_slab.argtypes = [_P, _I, ctypes.POINTER(Slab)]
+lib.pakv_layer_map_source.restype = _I
+lib.pakv_layer_map_source.argtypes = [_P, _I, ctypes.POINTER(_I)]
+lib.pakv_kv_bytes_per_token.restype = _I
+lib.pakv_kv_bytes_per_token.argtypes = [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+lib.pakv_slab_bytes.restype = _I
+lib.pakv_slab_bytes.argtypes = [_P, _I, _I, ctypes.POINTER(_S), ctypes.POINTER(_S)]
+lib.pakv_paged_kv_store.restype = _I
+lib.pakv_paged_kv_store.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _P]
+lib.pakv_decode_workspace_bytes.restype = _S
+lib.pakv_decode_workspace_bytes.argtypes = [_P, _I, _I, _I]
+lib.pakv_paged_attn_decode.restype = _I
+lib.pakv_paged_attn_decode.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _I, _I, _P, _S, _P]
+lib.pakv_paged_attn_extend.restype = _I
+lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
+
+
+class PakvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"pakv status {status}: {message}")
+        self.status = status
+
+
+def last_error():
+    return lib.pakv_last_error().decode()
+
+
+def _check(status):
+    if status != OK:
+        raise PakvError(status, last_error())
+    return status
+
+
+def _ptr(x):
+    """Device (or host) address of a tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def resolve_kv_sources(layer_types, first_shared):
+    n = len(layer_types)
+    types = (ctypes.c_int32 * max(n, 1))(*layer_types)
+    out = (ctypes.c_int32 * max(n, 1))()
+    _check(lib.pakv_resolve_kv_sources(n, ctypes.cast(types, _P), first_shared, ctypes.cast(out, _P)))
+    return list(out)[:n]
+
+
+class LayerMap:
+    """Owner of a pakv_layer_map*.  ``descs`` is a list of LayerDesc."""
+
+    def __init__(self, descs):
+        arr = (LayerDesc * len(descs))(*descs)
+        handle = _P()
+        _check(lib.pakv_layer_map_create(ctypes.cast(arr, _P), len(descs), ctypes.byref(handle)))
+        self.handle = handle
+        self.n = len(descs)
+        self._slabs = {}
+
+    def close(self):
+        if self.handle:
+            lib.pakv_layer_map_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def bind_slab(self, layer, k, v, num_pages, k_scale=None, v_scale=None):
+        slab = Slab(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), num_pages, PAGE_SIZE)
+        _check(lib.pakv_layer_map_bind_slab(self.handle, layer, ctypes.byref(slab)))
+        self._slabs[layer] = (k, v, k_scale, v_scale)   # keep the buffers alive
+
+    def source(self, layer):
+        out = _I()
+        _check(lib.pakv_layer_map_source(self.handle, layer, ctypes.byref(out)))
+        return out.value
+
+    def kv_bytes_per_token(self):
+        f, w = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.pakv_kv_bytes_per_token(self.handle, ctypes.byref(f), ctypes.byref(w)))
+        return f.value, w.value
+
+    def slab_bytes(self, layer, num_pages):
+        c, s = _S(), _S()
+        _check(lib.pakv_slab_bytes(self.handle, layer, num_pages, ctypes.byref(c), ctypes.byref(s)))
+        return c.value, s.value
+
+
+def make_pages(page_table, num_seqs=None, max_pages_per_seq=None):
+    """pakv_pages for a device int32 [B, max_pages] tensor."""
+    if num_seqs is None:
+        num_seqs, max_pages_per_seq = page_table.shape
+    return Pages(_ptr(page_table), num_seqs, max_pages_per_seq)
+
+
+def paged_kv_store(layer_map, layer, pages, cu_tokens, start_pos, k, v, num_seqs, total_tokens, stream=None):
+    return _check(lib.pakv_paged_kv_store(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_tokens),
+                                          _ptr(start_pos), _ptr(k), _ptr(v), num_seqs, total_tokens,
+                                          _stream(stream)))
+
+
+def decode_workspace_bytes(layer_map, layer, num_seqs, max_kv_len):
+    return lib.pakv_decode_workspace_bytes(layer_map.handle, layer, num_seqs, max_kv_len)
+
+
+def paged_attn_decode(layer_map, layer, pages, kv_lens, q, out, num_seqs, max_kv_len,
+                      workspace, workspace_bytes, stream=None):
+    return _check(lib.pakv_paged_attn_decode(layer_map.handle, layer, ctypes.byref(pages), _ptr(kv_lens),
+                                             _ptr(q), _ptr(out), num_seqs, max_kv_len, _ptr(workspace),
+                                             workspace_bytes, _stream(stream)))
+
+
+def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_seqs, total_q, max_q_len,
+                      max_kv_len, stream=None):
+    return _check(lib.pakv_paged_attn_extend(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
+                                             _ptr(prefix_lens), _ptr(q), _ptr(out), num_seqs, total_q,
+                                             max_q_len, max_kv_len, _stream(stream)))

@@ -1,0 +1,224 @@
+/*
+ * pakv.h -- paged KV-cache attention with per-layer mask regimes, for MI355X (gfx950).
+ *
+ * The calls follow how the pages state the problem:
+ *  - each layer that owns KV has its own paged cache; a KV-shared layer points at
+ *    its source layer's cache instead of holding one (unsloth commit dee9371,
+ *    "scripts": shared layers reference the store layer's PagedKVCache);
+ *  - one (layer, source) list decides which slab every layer reads, and a shared
+ *    layer with no earlier layer of its attention type is refused
+ *    (FreeToken PR #898, "perf(gemma4): read the source layer's kv slab on
+ *    kv-shared layers", description, first and second bullets, and the review);
+ *  - the store returns early for a shared layer, and the extend and decode
+ *    kernels find slabs and scales through the same mapping (same PR,
+ *    description, fourth and fifth bullets);
+ *  - two mask regimes: full layers are purely causal, sliding layers are causal
+ *    and keep key j for query p only while p - j < W, so the window counts the
+ *    query's own position (unsloth commit ca9dbce, the change that builds one
+ *    block mask per attention regime; pegainfer issue #807, Description, on
+ *    passing W - 1 to an API that measures an inclusive distance).  This
+ *    library takes W itself.
+ *
+ * Conventions shared by every call:
+ *  - No exceptions cross the ABI.  Every call returns a pakv_status; the text of
+ *    the last failure on the calling thread is available from pakv_last_error()
+ *    until that thread's next call.
+ *  - Argument errors are found on the host and returned before anything is
+ *    launched.  Nothing is launched either when a call has no work (zero tokens).
+ *  - Device pointers are plain device addresses owned by the caller.  The library
+ *    never allocates, frees or copies device memory, never synchronises, and
+ *    never reads device memory from the host: every call is asynchronous on the
+ *    stream it is given (a hipStream_t passed as void*; NULL is the null stream).
+ *  - bf16 tensors are 16-bit bfloat16 bit patterns.  Page size is 16 tokens.
+ *  - Device-side values (lengths, page ids) are clamped into range so that no
+ *    access leaves the buffers the descriptors describe: a length above the
+ *    stated bound or a page id outside [0, num_pages) never faults, but the
+ *    affected outputs are then unspecified.
+ *
+ * Slab layout (one slab per owning layer; K and V are separate buffers):
+ *   K codes : [num_pages][Hkv][16][D]  token-major inside a page
+ *   V codes : [num_pages][Hkv][D][16]  dim-major inside a page (each dim's 16
+ *             tokens are contiguous), so that the value contraction over tokens
+ *             reads contiguous runs
+ *   codes are bf16 (2 bytes) for PAKV_KV_BF16 and int8 for PAKV_KV_INT8_PTH.
+ *   int8 scales: k_scale, v_scale : float32 [num_pages][Hkv][16], one per token
+ *   and KV head (FreeToken PR #898, description bullet on the per-token-head
+ *   formats; "End to end": D + 4 bytes per row).
+ * Every (page, head) block is 16*D codes, contiguous.
+ *
+ * int8 per-token-head encoding (the pages do not print it; this library's
+ * reading): for a row x of D bf16 values, amax = max|x_d|, scale =
+ * fl32(amax / 127) by IEEE float32 division, code_d = clamp(rne(fl32(x_d /
+ * scale)), -127, 127); an all-zero row gets scale 0 and zero codes.  A stored
+ * element decodes to code * scale.
+ */
+#ifndef PAKV_H
+#define PAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAKV_PAGE_SIZE 16
+
+typedef enum {
+    PAKV_OK = 0,
+    PAKV_ERR_INVALID = 1,     /* a null pointer, a negative size, an index out of range */
+    PAKV_ERR_UNSUPPORTED = 2, /* a shape this build has no kernel for (head_dim, group size, page size) */
+    PAKV_ERR_ALIAS = 3,       /* a KV-sharing rule is broken (see pakv_layer_map_create) */
+    PAKV_ERR_WORKSPACE = 4,   /* decode workspace missing or too small */
+    PAKV_ERR_HIP = 5          /* the HIP runtime reported an error; the message carries its text */
+} pakv_status;
+
+typedef enum {
+    PAKV_KV_BF16 = 0,     /* bf16 codes */
+    PAKV_KV_INT8_PTH = 1  /* int8 codes + one float32 scale per token and KV head */
+} pakv_kv_dtype;
+
+/* Per-layer description.
+ *   head_dim      : 256 or 512
+ *   num_q_heads   : Hq; a multiple of num_kv_heads, with Hq / Hkv <= 16
+ *   num_kv_heads  : Hkv >= 1.  Query head h reads KV head h / (Hq / Hkv).
+ *   window        : 0 for a full (causal) layer; W > 0 for a sliding layer, where
+ *                   key position j is visible to query position p iff
+ *                   j <= p and p - j < W.
+ *   kv_source     : -1 if the layer owns a slab, else the index of the owning
+ *                   layer whose slab it reads.
+ *   kv_dtype      : a pakv_kv_dtype.
+ *   sm_scale      : softmax scale applied to q.k (for example 1/sqrt(head_dim)). */
+typedef struct {
+    int32_t head_dim;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t window;
+    int32_t kv_source;
+    int32_t kv_dtype;
+    float sm_scale;
+} pakv_layer_desc;
+
+/* Device buffers of one owning layer's slab (layout above).  k_scale / v_scale
+ * are NULL for bf16 slabs.  page_size must be 16. */
+typedef struct {
+    void* k;
+    void* v;
+    float* k_scale;
+    float* v_scale;
+    int32_t num_pages;
+    int32_t page_size;
+} pakv_slab;
+
+/* Page table shared by the layers of one batch: device int32
+ * [num_seqs][max_pages_per_seq]; entry [b][i] is the physical page holding
+ * positions 16*i .. 16*i + 15 of sequence b.  Owned by the caller. */
+typedef struct {
+    const int32_t* page_table;
+    int32_t num_seqs;
+    int32_t max_pages_per_seq;
+} pakv_pages;
+
+typedef struct pakv_layer_map pakv_layer_map;
+
+/* Text of the calling thread's last failure ("" if none).  Valid until the
+ * thread's next pakv_* call. */
+const char* pakv_last_error(void);
+
+/* Source rule for a model whose layers first_shared .. n_layers-1 are KV-shared
+ * (FreeToken PR #898, description, first bullet): such a layer reads the last
+ * layer before first_shared with the same layer_type (any int32 tag, for
+ * example 0 = sliding, 1 = full).  Layers below first_shared read themselves.
+ * Writes out_source[n_layers] (host memory).  first_shared >= n_layers means
+ * no sharing.  Returns PAKV_ERR_ALIAS, writing nothing, if a shared layer has
+ * no earlier layer of its type (the refusal asked for in that PR's review). */
+pakv_status pakv_resolve_kv_sources(int32_t n_layers, const int32_t* layer_type,
+                                    int32_t first_shared, int32_t* out_source);
+
+/* Builds the host-side map of n layers from descs (copied; host memory).
+ * Returns PAKV_ERR_ALIAS if some kv_source is not an earlier layer, is itself
+ * shared, or differs from the layer in head_dim, num_kv_heads, window or
+ * kv_dtype; PAKV_ERR_UNSUPPORTED for a head_dim other than 256 / 512 or a
+ * group size Hq / Hkv above 16; PAKV_ERR_INVALID for other bad fields.
+ * On success *out owns the map; release it with pakv_layer_map_destroy. */
+pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_layer_map** out);
+void pakv_layer_map_destroy(pakv_layer_map* map);
+
+/* Attaches a slab to an owning layer (the map keeps the pointers; the caller
+ * keeps ownership of the memory).  PAKV_ERR_ALIAS for a shared layer: a shared
+ * layer never has a slab of its own.  Rebinding replaces the previous slab. */
+pakv_status pakv_layer_map_bind_slab(pakv_layer_map* map, int32_t layer, const pakv_slab* slab);
+
+/* The layer whose slab `layer` reads (itself for an owner). */
+pakv_status pakv_layer_map_source(const pakv_layer_map* map, int32_t layer, int32_t* src);
+
+/* KV bytes per token over owning layers only (FreeToken PR #898, description,
+ * third bullet: only layers that own KV are priced), split into the full group
+ * (window == 0) and the window group: sum of Hkv * 2 * row, row = 2*D for bf16
+ * and D + 4 for int8 per-token-head. */
+pakv_status pakv_kv_bytes_per_token(const pakv_layer_map* map, int64_t* full_bytes, int64_t* window_bytes);
+
+/* Bytes of the K (or V) code buffer and of one scale buffer for a slab of
+ * num_pages pages of the given layer (scale bytes are 0 for bf16). */
+pakv_status pakv_slab_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_pages,
+                            size_t* code_bytes, size_t* scale_bytes);
+
+/* Writes new K/V rows into the slab of `layer`.
+ *   cu_tokens   : device int32 [num_seqs + 1], prefix sums; sequence b owns rows
+ *                 cu_tokens[b] .. cu_tokens[b+1]-1 of k and v
+ *   start_pos   : device int32 [num_seqs]; row i of sequence b goes to position
+ *                 start_pos[b] + i
+ *   k, v        : device bf16 [total_tokens][Hkv][D], token-major
+ * For an int8 layer the rows are encoded in-kernel (see the header comment).
+ * A shared layer returns PAKV_OK and launches nothing: its source stored the
+ * same rows earlier in the forward (FreeToken PR #898, description, fourth
+ * bullet).  Rows whose position falls outside the page table are dropped. */
+pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                const int32_t* cu_tokens, const int32_t* start_pos,
+                                const void* k, const void* v,
+                                int32_t num_seqs, int32_t total_tokens, void* stream);
+
+/* Workspace bytes pakv_paged_attn_decode needs for these sizes. */
+size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
+                                   int32_t num_seqs, int32_t max_kv_len);
+
+/* One decode query per sequence.
+ *   kv_lens     : device int32 [num_seqs], tokens stored for the sequence
+ *                 including the current one, 1 <= kv_lens[b] <= max_kv_len.
+ *                 The query sits at position kv_lens[b] - 1; its own K/V must
+ *                 already be stored (by this layer's source for a shared layer).
+ *   q, out      : device bf16 [num_seqs][Hq][D]
+ *   max_kv_len  : host upper bound on kv_lens, used to size the grid
+ *   workspace   : device memory of at least pakv_decode_workspace_bytes(...)
+ * A shared layer reads its source's slab (and scales) with its own descriptor
+ * (window, sm_scale, Hq).  The work of a sequence is cut into splits whose
+ * boundaries depend only on the layer, max_kv_len and the sequence's own
+ * length; partial results are merged in a fixed order, so the output is
+ * bit-identical from run to run and does not depend on page placement. */
+pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* kv_lens, const void* q, void* out,
+                                   int32_t num_seqs, int32_t max_kv_len,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chunked prefill: a chunk of new queries per sequence after a cached prefix.
+ *   cu_q        : device int32 [num_seqs + 1], prefix sums of chunk lengths n_b
+ *   prefix_lens : device int32 [num_seqs]; query i of sequence b sits at
+ *                 position prefix_lens[b] + i
+ *   q, out      : device bf16 [total_q][Hq][D], token-major, packed by cu_q
+ *   max_q_len   : host upper bound on n_b;  max_kv_len : host bound on
+ *                 prefix_lens[b] + n_b
+ * The chunk's own K/V must already be stored (by the source for a shared layer,
+ * as the source runs earlier in the forward); the kernel reads prefix and chunk
+ * from the slab.  bf16 layers only in this build (PAKV_ERR_UNSUPPORTED for
+ * int8). */
+pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* cu_q, const int32_t* prefix_lens,
+                                   const void* q, void* out,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                   int32_t max_kv_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAKV_H */

@@ -1,0 +1,198 @@
+"""Host-side checks of libpakv.so that need no GPU: every symbol the header
+declares is exported, the layer-map rules, the bytes-per-token figures the
+pages print (FreeToken PR #898, "End to end"), and argument errors that are
+returned before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from full_attention_amd import pakv
+from workloads import e2b_layer_types, e4b_layer_types
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pakv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pakv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("pakv_paged_kv_store", "pakv_paged_attn_decode", "pakv_paged_attn_extend",
+                     "pakv_layer_map_create", "pakv_resolve_kv_sources"):
+        assert required in names
+
+
+@pytest.mark.parametrize("name", declared_symbols())
+def test_every_declared_symbol_is_exported(name):
+    assert hasattr(pakv.lib, name)
+    assert name in pakv.EXPORTED
+
+
+def _desc(d=256, hq=8, hkv=1, w=0, src=-1, dtype=pakv.KV_BF16, scale=0.0625):
+    return pakv.LayerDesc(d, hq, hkv, w, src, dtype, scale)
+
+
+def _model(name, fmt, share):
+    types = e2b_layer_types() if name == "E2B" else e4b_layer_types()
+    first = 15 if name == "E2B" else 24
+    hkv = 1 if name == "E2B" else 2
+    tags = [1 if t == "full" else 0 for t in types]
+    src = pakv.resolve_kv_sources(tags, first if share else len(types))
+    dtype = pakv.KV_BF16 if fmt == "bf16" else pakv.KV_INT8_PTH
+    descs = []
+    for l, t in enumerate(types):
+        d, w = (512, 0) if t == "full" else (256, 512)
+        descs.append(_desc(d, 8, hkv, w, -1 if src[l] == l else src[l], dtype))
+    return pakv.LayerMap(descs), src, types
+
+
+def _golden_rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].split()
+        if line:
+            out.append(line)
+    return out
+
+
+@pytest.mark.parametrize("row", _golden_rows("freetoken_pr898_unit_bytes.txt"), ids=lambda r: "-".join(r[:3]))
+def test_library_bytes_per_token_match_printed(row):
+    m, _, _ = _model(row[0], row[1], row[2] == "shared")
+    assert m.kv_bytes_per_token() == (int(row[3]), int(row[4]))
+
+
+@pytest.mark.parametrize("model,full,sliding", [("E2B", 14, 13), ("E4B", 23, 22)])
+def test_library_source_rule_matches_printed(model, full, sliding):
+    m, src, types = _model(model, "bf16", True)
+    first = 15 if model == "E2B" else 24
+    for l, t in enumerate(types):
+        want = l if l < first else (full if t == "full" else sliding)
+        assert src[l] == want and m.source(l) == want
+
+
+def test_unsourced_shared_layer_refused():
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.resolve_kv_sources([0, 0, 1], 2)
+    assert e.value.status == pakv.ERR_ALIAS
+    assert "no earlier layer" in str(e.value)
+
+
+@pytest.mark.parametrize("descs,status", [
+    ([_desc(), _desc(src=2)], pakv.ERR_ALIAS),                        # source not earlier
+    ([_desc(), _desc(src=0), _desc(src=1)], pakv.ERR_ALIAS),          # source itself shared
+    ([_desc(d=256), _desc(d=512, src=0)], pakv.ERR_ALIAS),            # different head_dim
+    ([_desc(w=32), _desc(w=0, src=0)], pakv.ERR_ALIAS),               # different window
+    ([_desc(hkv=1), _desc(hkv=2, hq=8, src=0)], pakv.ERR_ALIAS),      # different Hkv
+    ([_desc(), _desc(src=0, dtype=pakv.KV_INT8_PTH)], pakv.ERR_ALIAS),  # different dtype
+    ([_desc(d=128)], pakv.ERR_UNSUPPORTED),
+    ([_desc(hq=7, hkv=2)], pakv.ERR_INVALID),
+    ([_desc(hq=32, hkv=1)], pakv.ERR_UNSUPPORTED),
+    ([_desc(w=-1)], pakv.ERR_INVALID),
+    ([_desc(scale=0.0)], pakv.ERR_INVALID),
+    ([_desc(dtype=7)], pakv.ERR_INVALID),
+])
+def test_layer_map_rules(descs, status):
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap(descs)
+    assert e.value.status == status
+
+
+def test_shared_layer_cannot_own_a_slab():
+    m = pakv.LayerMap([_desc(), _desc(src=0)])
+    with pytest.raises(pakv.PakvError) as e:
+        m.bind_slab(1, 0x1000, 0x2000, 4)
+    assert e.value.status == pakv.ERR_ALIAS
+    m.bind_slab(0, 0x1000, 0x2000, 4)        # host bookkeeping only; nothing is dereferenced
+    with pytest.raises(pakv.PakvError):
+        m.bind_slab(0, 0x1000, 0x2000, 0)
+    m8 = pakv.LayerMap([_desc(dtype=pakv.KV_INT8_PTH)])
+    with pytest.raises(pakv.PakvError):
+        m8.bind_slab(0, 0x1000, 0x2000, 4)    # int8 needs scales
+
+
+def test_slab_bytes():
+    m = pakv.LayerMap([_desc(d=512, hkv=2), _desc(d=256, hkv=1, dtype=pakv.KV_INT8_PTH)])
+    assert m.slab_bytes(0, 10) == (10 * 2 * 16 * 512 * 2, 0)
+    assert m.slab_bytes(1, 10) == (10 * 1 * 16 * 256, 10 * 16 * 4)
+
+
+def _bound_map():
+    m = pakv.LayerMap([_desc(), _desc(src=0), _desc(dtype=pakv.KV_INT8_PTH)])
+    m.bind_slab(0, 0x1000, 0x2000, 8)
+    m.bind_slab(2, 0x1000, 0x2000, 8, 0x3000, 0x4000)
+    return m
+
+
+def test_store_on_shared_layer_returns_ok_without_launch():
+    m = _bound_map()
+    pages = pakv.Pages(0x5000, 2, 4)
+    # null device pointers: a shared layer must return before touching anything
+    assert pakv.lib.pakv_paged_kv_store(m.handle, 1, ctypes.byref(pages), None, None, None, None, 2, 5, None) == 0
+
+
+def test_argument_errors_are_returned_before_launch():
+    m = _bound_map()
+    pages = pakv.Pages(0x5000, 2, 4)
+    lib = pakv.lib
+    # decode: null q
+    assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, None, 0x7000, 2, 40,
+                                      0x8000, 1 << 20, None) == pakv.ERR_INVALID
+    # decode: length bound beyond the page table (4 pages = 64 positions)
+    assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 2, 65,
+                                      0x8000, 1 << 20, None) == pakv.ERR_INVALID
+    # decode: workspace too small
+    need = lib.pakv_decode_workspace_bytes(m.handle, 0, 2, 40)
+    assert need > 0
+    assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 2, 40,
+                                      0x8000, need - 1, None) == pakv.ERR_WORKSPACE
+    assert "workspace" in pakv.last_error()
+    # decode: more sequences than the page table holds
+    assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 3, 40,
+                                      0x8000, 1 << 20, None) == pakv.ERR_INVALID
+    # decode: no sequences -> nothing to do
+    assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), None, None, None, 0, 40,
+                                      None, 0, None) == pakv.OK
+    # extend on an int8 layer is not built
+    assert lib.pakv_paged_attn_extend(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x7000,
+                                      2, 10, 5, 40, None) == pakv.ERR_UNSUPPORTED
+    # extend: empty chunk -> nothing to do
+    assert lib.pakv_paged_attn_extend(m.handle, 0, ctypes.byref(pages), None, None, None, None,
+                                      2, 0, 0, 40, None) == pakv.OK
+    # store: unbound layer map entry / bad layer index
+    assert lib.pakv_paged_kv_store(m.handle, 9, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x6300,
+                                   2, 5, None) == pakv.ERR_INVALID
+    # store: null k
+    assert lib.pakv_paged_kv_store(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, None, 0x6300,
+                                   2, 5, None) == pakv.ERR_INVALID
+
+
+def test_unbound_source_slab_is_an_error():
+    m = pakv.LayerMap([_desc(), _desc(src=0)])
+    pages = pakv.Pages(0x5000, 1, 4)
+    st = pakv.lib.pakv_paged_attn_decode(m.handle, 1, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 1, 40,
+                                         0x8000, 1 << 20, None)
+    assert st == pakv.ERR_INVALID and "not bound" in pakv.last_error()
+
+
+def test_workspace_grows_with_splits():
+    m = pakv.LayerMap([_desc(d=512), _desc(d=256, w=512)])
+    a = pakv.decode_workspace_bytes(m, 0, 64, 4097)
+    b = pakv.decode_workspace_bytes(m, 0, 64, 131073)
+    assert 0 < a < b
+    # a sliding layer's split count is bounded by its window, not the context
+    assert pakv.decode_workspace_bytes(m, 1, 8, 131073) == pakv.decode_workspace_bytes(m, 1, 8, 4097)
+
+
+def test_one_hip_runtime_per_process():
+    """The library must bind to the HIP runtime torch loaded (same soname), not
+    load a second one: torch's streams are only valid in its own runtime."""
+    maps = open("/proc/self/maps").read()
+    runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes

@@ -1,0 +1,146 @@
+"""paged_attn_decode on the GPU against the oracle, within |err| <= 2e-2 + 1e-2|ref|
+(bf16 outputs, fp32 accumulation), plus the exact properties the method has:
+W = 1 returns the query's own value row; outputs are bit-identical from run to
+run, across page placements and across batch compositions; a shared layer's
+output is bit-identical to its source's and a shared sliding layer keeps its
+window.  Unwritten slots hold NaN throughout."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import LayerSpec, bf16_to_f32
+
+from gpu_helpers import Scenario, assert_close, dev_bits, host_bits, i32, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(d, hq, hkv, window, kv_dtype, lens, seed, only_visible=True):
+    kind = "sliding" if window else "full"
+    spec = LayerSpec(kind, d, hq, hkv, window, kv_dtype=kv_dtype)
+    sc = Scenario([spec], None, lens, seed=seed)
+    starts = [max(0, L - window) if (window and only_visible) else 0 for L in lens]
+    counts = [L - s for L, s in zip(lens, starts)]
+    sc.store(0, starts, counts)
+    return sc
+
+
+LENS = [1, 2, 15, 16, 17, 31, 33, 100, 129, 257, 700]
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 8), (16, 2), (4, 4), (16, 1)])
+@pytest.mark.parametrize("window", [0, 1, 7, 32, 512])
+def test_decode_matches_oracle(kv_dtype, d, hq, hkv, window):
+    need_gpu()
+    seed = zlib.crc32(repr((kv_dtype, d, hq, hkv, window)).encode()) % 10000
+    sc = _decode_case(d, hq, hkv, window, kv_dtype, LENS, seed)
+    got, ref, _ = sc.decode(0, LENS)
+    assert_close(got, ref, f"decode d={d} hq={hq} hkv={hkv} W={window} {kv_dtype}")
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_window_one_returns_own_value_row(d):
+    need_gpu()
+    lens = [1, 5, 16, 17, 300]
+    sc = _decode_case(d, 8, 1, 1, "bf16", lens, seed=5)
+    got, _, _ = sc.decode(0, lens)
+    k, v, cu, starts = sc.rows[0]
+    for b, L in enumerate(lens):
+        own = v[cu[b + 1] - 1, 0]            # row of position L - 1
+        assert np.array_equal(got[b], np.broadcast_to(own, got[b].shape))
+
+
+def test_long_context_many_splits():
+    need_gpu()
+    lens = [9000, 40000, 3]
+    for kv_dtype in ("bf16", "int8"):
+        sc = _decode_case(512, 8, 1, 0, kv_dtype, lens, seed=9)
+        got, ref, _ = sc.decode(0, lens)
+        assert_close(got, ref, f"long {kv_dtype}")
+
+
+def test_deterministic_and_page_placement_invariant():
+    need_gpu()
+    lens = [37, 1000, 513, 4096]
+    outs = []
+    for pool_seed in (1, 2):
+        spec = LayerSpec("full", 512, 8, 1, 0)
+        sc = Scenario([spec], None, lens, seed=100)
+        # same draws, different page permutation: re-seed the pool only
+        rng = np.random.default_rng(pool_seed)
+        from workloads import make_page_pool
+        sc.pool = make_page_pool(rng, lens, spare=4 + pool_seed)
+        from full_attention_amd.cache import PagedKVCache
+        sc.cache = PagedKVCache([spec], None, sc.pool.num_pages)
+        sc.cache.set_page_table(sc.pool.page_table)
+        sc.store(0, [0] * 4, lens)
+        q = np.random.default_rng(7).standard_normal((4, 8, 512)).astype(np.float32)
+        from workloads import bf16_from_f32
+        qb = dev_bits(bf16_from_f32(q))
+        a = host_bits(sc.cache.decode(0, i32(lens), qb, 4096))
+        b = host_bits(sc.cache.decode(0, i32(lens), qb, 4096))
+        assert np.array_equal(a, b)
+        outs.append(a)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_batch_composition_does_not_change_a_sequence():
+    need_gpu()
+    spec = LayerSpec("sliding", 256, 8, 1, 512)
+    lens = [2000, 777, 3000]
+    sc = Scenario([spec], None, lens, seed=12)
+    sc.store(0, [0, 0, 0], lens)
+    from workloads import normal_bf16
+    q = normal_bf16(np.random.default_rng(3), (3, 8, 256))
+    full = host_bits(sc.cache.decode(0, i32(lens), dev_bits(q), 3000))
+    # the same sequence 1 alone (its page-table row moved to the front)
+    from full_attention_amd import pakv
+    table = torch.as_tensor(sc.pool.page_table[1:2], dtype=torch.int32).cuda()
+    saved = sc.cache.pages
+    sc.cache.pages = pakv.make_pages(table)
+    alone = host_bits(sc.cache.decode(0, i32([777]), dev_bits(q[1:2]), 3000))
+    sc.cache.pages = saved
+    assert np.array_equal(full[1:2], alone)
+
+
+def test_shared_layers_read_their_source():
+    need_gpu()
+    specs = [LayerSpec("sliding", 256, 8, 1, 64), LayerSpec("full", 512, 8, 1, 0),
+             LayerSpec("sliding", 256, 8, 1, 64), LayerSpec("full", 512, 8, 1, 0)]
+    lens = [300, 65, 64, 1]
+    sc = Scenario(specs, 2, lens, seed=44)
+    for layer in range(4):
+        sc.store(layer, [0] * 4, lens)
+    from workloads import normal_bf16
+    for src, shared in ((0, 2), (1, 3)):
+        q = dev_bits(normal_bf16(sc.rng, (4, 8, specs[src].head_dim)))
+        a = host_bits(sc.cache.decode(src, i32(lens), q, 300))
+        b = host_bits(sc.cache.decode(shared, i32(lens), q, 300))
+        assert np.array_equal(a, b)
+    # the shared sliding layer keeps its window: differs from full attention over the same rows
+    got, ref, q = sc.decode(2, lens)
+    assert_close(got, ref, "shared sliding")
+    from oracle import attend
+    k, v, cu, _ = sc.rows[0]
+    qf = bf16_to_f32(q).astype(np.float64)
+    kf = bf16_to_f32(k).astype(np.float64)
+    vf = bf16_to_f32(v).astype(np.float64)
+    full = attend(qf[0:1], np.array([299]), kf[:300], vf[:300], np.arange(300), 0, specs[2].sm_scale)
+    assert np.abs(bf16_to_f32(got[0]) - full[0]).max() > 0.05
+
+
+def test_unwritten_slots_do_not_leak_into_sliding_output():
+    need_gpu()
+    # only the visible rows are written; everything before the window is NaN
+    lens = [1000, 1030, 17]
+    sc = _decode_case(256, 8, 1, 32, "bf16", lens, seed=77, only_visible=True)
+    got, ref, _ = sc.decode(0, lens)
+    assert_close(got, ref, "sentinel")
+    sc8 = _decode_case(512, 8, 1, 32, "int8", lens, seed=78, only_visible=True)
+    got, ref, _ = sc8.decode(0, lens)
+    assert_close(got, ref, "sentinel int8")

@@ -1,0 +1,58 @@
+"""paged_attn_extend on the GPU against the oracle (chunked prefill after a
+cached prefix; the chunk is stored first and read back from the pages)."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import LayerSpec, normal_bf16
+
+from gpu_helpers import Scenario, assert_close, dev_bits, host_bits, i32, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _extend_case(d, hq, hkv, window, prefixes, chunks, seed):
+    kind = "sliding" if window else "full"
+    spec = LayerSpec(kind, d, hq, hkv, window)
+    caps = [p + n for p, n in zip(prefixes, chunks)]
+    sc = Scenario([spec], None, [max(c, 1) for c in caps], seed=seed)
+    sc.store(0, [0] * len(caps), caps)
+    return sc
+
+
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 8), (16, 2), (3, 1)])
+@pytest.mark.parametrize("window", [0, 1, 5, 32])
+def test_extend_matches_oracle(d, hq, hkv, window):
+    need_gpu()
+    prefixes = [0, 17, 100, 5, 64]
+    chunks = [64, 33, 1, 0, 70]
+    sc = _extend_case(d, hq, hkv, window, prefixes, chunks, seed=zlib.crc32(repr((d, hq, hkv, window)).encode()) % 1000)
+    for got, ref, b in sc.extend(0, prefixes, chunks):
+        assert_close(got, ref, f"extend d={d} hq={hq} hkv={hkv} W={window} seq {b}")
+
+
+def test_extend_window_one_returns_own_value_row():
+    need_gpu()
+    prefixes, chunks = [3, 40], [20, 9]
+    sc = _extend_case(512, 8, 1, 1, prefixes, chunks, seed=8)
+    pairs = sc.extend(0, prefixes, chunks)
+    k, v, cu, _ = sc.rows[0]
+    for got, _, b in pairs:
+        for i in range(chunks[b]):
+            own = v[cu[b] + prefixes[b] + i, 0]
+            assert np.array_equal(got[i], np.broadcast_to(own, got[i].shape))
+
+
+def test_extend_deterministic():
+    need_gpu()
+    prefixes, chunks = [0, 300], [200, 129]
+    sc = _extend_case(256, 8, 1, 64, prefixes, chunks, seed=3)
+    q = dev_bits(normal_bf16(sc.rng, (329, 8, 256)))
+    cu = i32([0, 200, 329])
+    a = host_bits(sc.cache.extend(0, cu, i32(prefixes), q, 200, 429))
+    b = host_bits(sc.cache.extend(0, cu, i32(prefixes), q, 200, 429))
+    assert np.array_equal(a, b)
