@@ -1,0 +1,437 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-attention hot path on one MI355X.
+
+Headline (the JSON line's ``value``): one decode step of an E2B-like stack --
+35 layers (28 sliding, D 256, W 512; 7 full, D 512), Hq 8, Hkv 1, layers 15-34
+KV-shared (15 slabs), batch 64, cached lengths uniform in [512, 4096], page size
+16 over a permuted pool.  A step stores the new token's K/V on the 15 owning
+layers (shared layers store nothing) and runs decode on all 35 layers.  The
+step is captured once into a HIP graph and replayed, as a serving engine does
+for its decode step.  ``value`` = algorithmic decode bytes per step (visible
+K/V rows once per sequence and KV head, plus Q and O) / step time, in GB/s.
+
+Also reported on the same line:
+* ``roofline``: the kernel with the largest total time in the step, its
+  algorithmic bytes per launch over its mean launch duration, measured with
+  HIP events the library records around each launch (pakv_set_timing_events),
+  against 8 TB/s;
+* ``extend``: the chunked-prefill stack on the same 35 layers (4 sequences,
+  cached prefixes 0 / 1024 / 2048 / 4096, 2048-token chunks stored through
+  paged_kv_store on the owning layers), in TFLOP/s of visible (query, key)
+  pairs (4 * D flops per pair and query head), with its own roofline against
+  2.5 PFLOP/s dense bf16;
+* ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
+  same decode workload, same byte count per unit.
+
+Inputs are synthetic: seeded N(0, 1) draws rounded to bf16, generated on the
+device with torch's generator for the large slabs (data generation is not
+timed).  Only --gpus 1 is supported.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "paged-attn decode GB/s (% HBM peak); extend TFLOP/s (% bf16 MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extend-steps", type=int, default=3)
+    ap.add_argument("--no-extend", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
+    ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of a graph")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+
+class DeviceDraws:
+    """Seeded N(0, 1) draws rounded to bf16 on the device (torch generator)."""
+
+    def __init__(self, torch, seed):
+        self.torch = torch
+        self.gen = torch.Generator(device="cuda")
+        self.gen.manual_seed(seed)
+
+    def bf16(self, shape):
+        t = self.torch
+        x = t.randn(shape, generator=self.gen, device="cuda", dtype=t.float32)
+        return x.to(t.bfloat16).view(t.int16)
+
+
+def i32(torch, x):
+    return torch.tensor(np.asarray(x, dtype=np.int32), dtype=torch.int32, device="cuda")
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "full_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    rec = data.get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timing:
+    """Event pairs handed to the library's timing hook."""
+
+    def __init__(self, torch, pakv, n_pairs):
+        import ctypes
+        self.torch, self.pakv = torch, pakv
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_pairs)]
+        for e in self.events:        # torch creates the HIP event on first record
+            e.record()
+        torch.cuda.synchronize()
+        self.handles = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+
+    def arm(self, mask):
+        self.pakv.set_timing_events(self.handles, mask)
+
+    def disarm(self):
+        used = self.pakv.timing_pairs_used()
+        self.pakv.set_timing_events(None, 0)
+        return used
+
+    def durations_ms(self, n):
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
+
+
+# ------------------------------------------------------------------ decode workload
+
+def setup_decode(torch):
+    from full_attention_amd.cache import PagedKVCache
+    from workloads import e2b_decode_workload, make_page_pool
+
+    wl = e2b_decode_workload()
+    B = wl.num_seqs
+    L = np.array(wl.cached_lens, dtype=np.int64)          # cached before the step
+    kv_len = L + 1                                         # the new token is stored first
+    rng = np.random.default_rng(wl.seed)
+    pool = make_page_pool(rng, kv_len)
+    cache = PagedKVCache(wl.layers, wl.first_shared, pool.num_pages, sentinel=True)
+    cache.set_page_table(pool.page_table)
+    draws = DeviceDraws(torch, wl.seed)
+    layers = wl.layers
+    owners = [l for l in range(len(layers)) if cache.sources[l] == l]
+    # cached rows: full layers hold every position; sliding layers only the
+    # positions the step's query can see (the rest keep the NaN sentinel)
+    for l in owners:
+        s = layers[l]
+        lo = np.maximum(0, kv_len - s.window) if s.window else np.zeros(B, np.int64)
+        counts = L - lo
+        cu = np.concatenate([[0], np.cumsum(counts)])
+        k = draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
+        v = draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
+        cache.store(l, i32(torch, cu), i32(torch, lo), k, v)
+        del k, v
+    new_k, new_v, q, out = {}, {}, [], []
+    for l, s in enumerate(layers):
+        if l in owners:
+            new_k[l] = draws.bf16((B, s.num_kv_heads, s.head_dim))
+            new_v[l] = draws.bf16((B, s.num_kv_heads, s.head_dim))
+        q.append(draws.bf16((B, s.num_q_heads, s.head_dim)))
+        out.append(torch.empty_like(q[-1]))
+    torch.cuda.synchronize()
+    st = dict(wl=wl, cache=cache, layers=layers, owners=owners, B=B, L=L, kv_len=kv_len,
+              cu_new=i32(torch, np.arange(B + 1)), pos_new=i32(torch, L), kv_len_t=i32(torch, kv_len),
+              max_kv_len=int(kv_len.max()), new_k=new_k, new_v=new_v, q=q, out=out, pool=pool)
+    # one workspace big enough for every layer, allocated before any capture
+    need = max(cache.workspace(l, B, st["max_kv_len"])[1] for l in range(len(layers)))
+    cache._workspace = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    return st
+
+
+def decode_step(st):
+    cache = st["cache"]
+    for l in range(len(st["layers"])):
+        if l in st["new_k"]:
+            cache.store(l, st["cu_new"], st["pos_new"], st["new_k"][l], st["new_v"][l])
+        cache.decode(l, st["kv_len_t"], st["q"][l], st["max_kv_len"], out=st["out"][l])
+
+
+def decode_bytes(st):
+    """Algorithmic bytes per layer: each visible K/V row once per (sequence, KV
+    head), plus Q read and O written."""
+    per_layer = []
+    for s in st["layers"]:
+        vis = np.minimum(st["kv_len"], s.window) if s.window else st["kv_len"]
+        row = 2 * s.head_dim if s.kv_dtype == "bf16" else s.head_dim + 4
+        kv = int(vis.sum()) * s.num_kv_heads * 2 * row
+        qo = 2 * st["B"] * s.num_q_heads * s.head_dim * 2
+        per_layer.append((kv, qo))
+    return per_layer
+
+
+# ------------------------------------------------------------------ extend workload
+
+def setup_extend(torch):
+    from full_attention_amd.cache import PagedKVCache
+    from workloads import e2b_extend_workload, make_page_pool
+
+    wl = e2b_extend_workload()
+    P = np.array(wl.cached_lens, dtype=np.int64)
+    n = np.array(wl.extend_lens, dtype=np.int64)
+    B = len(P)
+    rng = np.random.default_rng(wl.seed)
+    pool = make_page_pool(rng, P + n)
+    cache = PagedKVCache(wl.layers, wl.first_shared, pool.num_pages, sentinel=True)
+    cache.set_page_table(pool.page_table)
+    draws = DeviceDraws(torch, wl.seed)
+    layers = wl.layers
+    owners = [l for l in range(len(layers)) if cache.sources[l] == l]
+    cu_n = np.concatenate([[0], np.cumsum(n)])
+    chunk_k, chunk_v, q, out = {}, {}, [], []
+    for l in owners:
+        s = layers[l]
+        lo = np.maximum(0, P - s.window + 1) if s.window else np.zeros(B, np.int64)
+        counts = P - lo
+        if counts.sum() > 0:
+            cu = np.concatenate([[0], np.cumsum(counts)])
+            k = draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
+            v = draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
+            cache.store(l, i32(torch, cu), i32(torch, lo), k, v)
+        chunk_k[l] = draws.bf16((int(cu_n[-1]), s.num_kv_heads, s.head_dim))
+        chunk_v[l] = draws.bf16((int(cu_n[-1]), s.num_kv_heads, s.head_dim))
+    for s in layers:
+        q.append(draws.bf16((int(cu_n[-1]), s.num_q_heads, s.head_dim)))
+        out.append(torch.empty_like(q[-1]))
+    torch.cuda.synchronize()
+    return dict(wl=wl, cache=cache, layers=layers, owners=owners, B=B, P=P, n=n,
+                cu_t=i32(torch, cu_n), P_t=i32(torch, P), chunk_k=chunk_k, chunk_v=chunk_v, q=q, out=out,
+                max_q=int(n.max()), max_kv=int((P + n).max()))
+
+
+def extend_step(st):
+    cache = st["cache"]
+    for l in range(len(st["layers"])):
+        if l in st["chunk_k"]:
+            cache.store(l, st["cu_t"], st["P_t"], st["chunk_k"][l], st["chunk_v"][l])
+        cache.extend(l, st["cu_t"], st["P_t"], st["q"][l], st["max_q"], st["max_kv"], out=st["out"][l])
+
+
+def extend_flops(st):
+    """Per layer: 4 * D * Hq flops per visible (query, key) pair."""
+    out = []
+    for s in st["layers"]:
+        pairs = 0
+        for p, n in zip(st["P"], st["n"]):
+            pos = np.arange(p, p + n)
+            vis = pos + 1 if not s.window else np.minimum(pos + 1, s.window)
+            pairs += int(vis.sum())
+        out.append(4 * s.head_dim * s.num_q_heads * pairs)
+    return out
+
+
+# ------------------------------------------------------------------ timing
+
+def run_graph_or_eager(torch, step, steps, warmup, eager):
+    """Returns (ms per step, graph or None).  Steps are timed back to back,
+    bracketed by synchronisations."""
+    if eager:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps, None
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, g
+
+
+def kernel_durations(torch, pakv, step, n_launch_per_step, mask, steps):
+    """Mean duration (ms) of each selected launch in a step, over `steps`
+    eager steps.  The library launches each selected kernel through
+    hipExtLaunchKernelGGL with a caller event pair, so the dispatch itself
+    records start and stop: host-side gaps between launches are not counted."""
+    timing = Timing(torch, pakv, n_launch_per_step * steps)
+    torch.cuda.synchronize()
+    timing.arm(mask)
+    try:
+        for _ in range(steps):
+            step()
+    finally:
+        used = timing.disarm()
+    torch.cuda.synchronize()
+    assert used == n_launch_per_step * steps, (used, n_launch_per_step, steps)
+    d = np.array(timing.durations_ms(used)).reshape(steps, n_launch_per_step)
+    return d.mean(axis=0), "hipExtLaunchKernelGGL events, eager steps"
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(st, budget_s):
+    """The float64 oracle (attend over logical rows) on the decode workload,
+    layer by layer and sequence by sequence in step order, until about
+    budget_s seconds of oracle time (or the whole step).  Rows are fresh numpy
+    draws of the same shapes (timing only; no parity is claimed from this
+    leg).  Throughput counts the same algorithmic bytes as the GPU line."""
+    from oracle import attend, decode_positions
+    from workloads import bf16_to_f32, normal_bf16
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:
+        blas = []
+    rng = np.random.default_rng(7)
+    layers = st["layers"]
+    done_bytes, spent, units = 0, 0.0, 0
+    for l, s in enumerate(layers):
+        for b in range(st["B"]):
+            n = int(st["kv_len"][b])
+            lo = max(0, n - s.window) if s.window else 0
+            pos = np.arange(lo, n)
+            kr = bf16_to_f32(normal_bf16(rng, (len(pos), 1, s.head_dim))).astype(np.float64)
+            vr = bf16_to_f32(normal_bf16(rng, (len(pos), 1, s.head_dim))).astype(np.float64)
+            qv = bf16_to_f32(normal_bf16(rng, (1, s.num_q_heads, s.head_dim))).astype(np.float64)
+            t0 = time.perf_counter()
+            attend(qv, decode_positions(n), kr, vr, pos, s.window, s.sm_scale)
+            spent += time.perf_counter() - t0
+            units += 1
+            done_bytes += len(pos) * s.num_kv_heads * 2 * 2 * s.head_dim + 2 * s.num_q_heads * s.head_dim * 2
+        if spent > budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    threads = max([t for _, t in blas if t] or [1])
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"float64 oracle attend() on {units} (layer, sequence) decode units of the same "
+                       f"workload in step order ({units // st['B']} of 35 layers x 64 sequences); "
+                       f"{spent:.1f} s of oracle time; host affinity {cores} cores; BLAS {blas}")}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence, with no exchange for decode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from full_attention_amd import pakv
+
+    torch.cuda.set_device(0)
+    st = setup_decode(torch)
+    nl = len(st["layers"])
+    ms_step, graph = run_graph_or_eager(torch, lambda: decode_step(st), args.steps, args.warmup, args.eager)
+    per_layer = decode_bytes(st)
+    step_bytes = sum(kv + qo for kv, qo in per_layer)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # per-kernel durations of the decode partial pass (one launch per layer)
+    ksteps = max(1, min(args.steps, 10))
+    mean_ms, method = kernel_durations(torch, pakv, lambda: decode_step(st), nl, pakv.TIME_DECODE, ksteps)
+    groups = {}
+    for l, s in enumerate(st["layers"]):
+        key = f"decode_kernel<{s.head_dim},{'int8' if s.kv_dtype == 'int8' else 'bf16'}>"
+        g = groups.setdefault(key, {"ms": 0.0, "launches": 0, "bytes": 0})
+        g["ms"] += float(mean_ms[l])
+        g["launches"] += 1
+        g["bytes"] += per_layer[l][0] + per_layer[l][1]          # K/V rows + Q read + O written
+    dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
+    achieved = dom["bytes"] / dom["launches"] / (dom["ms"] / dom["launches"] * 1e-3) / 1e9
+    wl_name = "E2B-like decode, 35 layers, batch 64"
+    traffic = load_traffic(dom_name, wl_name, source_hash("kernels_decode.hip", "device_common.h"))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom_name, "launches_per_step": dom["launches"],
+                "mean_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2), "timing": method,
+                "algorithmic_bytes_per_launch": int(dom["bytes"] / dom["launches"]),
+                "per_kernel_us_per_step": {k: round(v["ms"] * 1e3, 1) for k, v in groups.items()}}
+
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) rounded to bf16; random page permutation)",
+            "config": {"workload": wl_name + " (28 sliding D256 W512 + 7 full D512; Hq 8, Hkv 1; "
+                                   "layers 15-34 KV-shared, 15 slabs; context U[512,4096]; page 16)",
+                       "global_batch": st["B"], "seq_len": int(st["max_kv_len"]),
+                       "layers": nl, "step": "store new K/V on 15 owners + decode 35 layers",
+                       "launch": "eager" if args.eager else "HIP graph replay",
+                       "algorithmic_bytes_per_step": int(step_bytes)},
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "roofline": roofline}
+    del graph
+
+    if not args.no_extend:
+        ex = setup_extend(torch)
+        ms_ex, g2 = run_graph_or_eager(torch, lambda: extend_step(ex), args.extend_steps, 1, True)
+        flops = extend_flops(ex)
+        tflops = sum(flops) / (ms_ex * 1e-3) / 1e12
+        mean_ex, emethod = kernel_durations(torch, pakv, lambda: extend_step(ex), nl, pakv.TIME_EXTEND, 1)
+        eg = {}
+        for l, s in enumerate(ex["layers"]):
+            key = f"extend_kernel<{s.head_dim}>"
+            g = eg.setdefault(key, {"ms": 0.0, "launches": 0, "flops": 0})
+            g["ms"] += float(mean_ex[l])
+            g["launches"] += 1
+            g["flops"] += flops[l]
+        en, e = max(eg.items(), key=lambda kv: kv[1]["ms"])
+        ach = e["flops"] / (e["ms"] * 1e-3) / 1e12
+        line["extend"] = {
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_ex, 3),
+            "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "config": {"workload": "E2B-like extend, 35 layers, 4 sequences, prefixes 0/1024/2048/4096, "
+                                   "2048-token chunks stored on the 15 owners", "flops_per_step": int(sum(flops))},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": en, "launches_per_step": e["launches"], "timing": emethod,
+                         "mean_launch_us": round(e["ms"] / e["launches"] * 1e3, 1),
+                         "algorithmic_flops_per_launch": int(e["flops"] / e["launches"]),
+                         "per_kernel_us_per_step": {k: round(v["ms"] * 1e3, 1) for k, v in eg.items()}}}
+        del ex
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,7 +76,8 @@ class PagedKVCache:
     def workspace(self, layer, num_seqs, max_kv_len):
         need = pakv.decode_workspace_bytes(self.map, layer, num_seqs, max_kv_len)
         if self._workspace is None or self._workspace.numel() < need:
-            self._workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            # zero-filled before first use; the library leaves it zeroed
+            self._workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._workspace, need
 
     def decode(self, layer, kv_lens, q, max_kv_len, out=None, stream=None):

@@ -24,6 +24,7 @@
 // NaN) contribute nothing.
 
 #include "device_common.h"
+#include "launch_timing.h"
 #include "pakv_internal.h"
 
 using namespace pakv_dev;
@@ -241,8 +242,8 @@ int launch_extend(const ExtendLaunch& s, void* stream) {
     const int64_t rows = (int64_t)s.max_q_len * a.group;
     dim3 grid((unsigned)((rows + kRowsPerWG - 1) / kRowsPerWG), s.hkv, s.num_seqs);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (s.head_dim == 256) hipLaunchKernelGGL(extend_kernel<256>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(extend_kernel<512>, grid, dim3(256), 0, st, a);
+    if (s.head_dim == 256) launch(PAKV_TIME_EXTEND, extend_kernel<256>, grid, dim3(256), 0, st, a);
+    else launch(PAKV_TIME_EXTEND, extend_kernel<512>, grid, dim3(256), 0, st, a);
     return (int)hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 // row lands as D strided 2-byte (or 1-byte) stores.
 
 #include "device_common.h"
+#include "launch_timing.h"
 #include "pakv_internal.h"
 
 using namespace pakv_dev;
@@ -33,17 +34,28 @@ struct StoreArgs {
     int32_t hkv;
 };
 
+// Sequence of token t: the last b with cu_tokens[b] <= t, found by the 64 lanes
+// of a wavefront together (each round narrows the range 64-fold).
+__device__ __forceinline__ int32_t find_seq(const int32_t* cu, int32_t num_seqs, int32_t t, int lane) {
+    int32_t lo = 0, n = num_seqs;           // answer in [lo, lo + n)
+    while (n > 1) {
+        const int32_t stride = (n + 63) / 64;
+        const int32_t idx = lo + lane * stride;
+        const bool le = (idx < lo + n) && (cu[idx] <= t);
+        const uint64_t m = __ballot(le);
+        const int last = m ? 63 - __builtin_clzll(m) : 0;
+        const int32_t end = lo + n;
+        lo += last * stride;
+        n = min(stride, end - lo);
+    }
+    return lo;
+}
+
 // Physical row address of (token t, head h), or false if the row falls outside
 // the page table or the pool.
-__device__ __forceinline__ bool locate(const StoreArgs& a, int32_t t, int32_t h,
+__device__ __forceinline__ bool locate(const StoreArgs& a, int32_t t, int32_t h, int lane,
                                        int64_t& page_head, int32_t& slot) {
-    // largest b with cu_tokens[b] <= t
-    int32_t lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-        int32_t mid = (lo + hi + 1) >> 1;
-        if (a.cu_tokens[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int32_t b = lo;
+    const int32_t b = find_seq(a.cu_tokens, a.num_seqs, t, lane);
     const int32_t pos = a.start_pos[b] + (t - a.cu_tokens[b]);
     if (pos < 0) return false;
     const int32_t pg = pos >> 4;
@@ -62,9 +74,7 @@ __global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
     const int32_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int32_t h = blockIdx.y;
     if (t >= a.total_tokens) return;
-    int64_t ph;
-    int32_t slot;
-    if (!locate(a, t, h, ph, slot)) return;
+    // the row itself does not depend on where it goes: fetch it first
     const int64_t src = ((int64_t)t * a.hkv + h) * D + lane * EPL;
     uint16_t kv[EPL], vv[EPL];
     if constexpr (EPL == 8) {
@@ -74,6 +84,9 @@ __global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
         *reinterpret_cast<u32x2*>(kv) = *reinterpret_cast<const u32x2*>(a.k + src);
         *reinterpret_cast<u32x2*>(vv) = *reinterpret_cast<const u32x2*>(a.v + src);
     }
+    int64_t ph;
+    int32_t slot;
+    if (!locate(a, t, h, lane, ph, slot)) return;
     uint16_t* kdst = reinterpret_cast<uint16_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
     if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(kdst) = *reinterpret_cast<u32x4*>(kv);
     else *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kv);
@@ -109,9 +122,6 @@ __global__ __launch_bounds__(256) void store_int8_kernel(StoreArgs a) {
     const int32_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int32_t h = blockIdx.y;
     if (t >= a.total_tokens) return;
-    int64_t ph;
-    int32_t slot;
-    if (!locate(a, t, h, ph, slot)) return;
     const int64_t src = ((int64_t)t * a.hkv + h) * D + lane * EPL;
     float kx[EPL], vx[EPL];
     float kmax = 0.0f, vmax = 0.0f;
@@ -122,6 +132,9 @@ __global__ __launch_bounds__(256) void store_int8_kernel(StoreArgs a) {
         kmax = fmaxf(kmax, fabsf(kx[e]));
         vmax = fmaxf(vmax, fabsf(vx[e]));
     }
+    int64_t ph;
+    int32_t slot;
+    if (!locate(a, t, h, lane, ph, slot)) return;
     kmax = wave_max(kmax);
     vmax = wave_max(vmax);
     const float ks = kmax / 127.0f;   // IEEE division (no fast-math in this build)
@@ -163,12 +176,13 @@ int launch_store(const StoreLaunch& s, void* stream) {
     a.hkv = s.hkv;
     dim3 grid((s.total_tokens + 3) / 4, s.hkv);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int K = PAKV_TIME_STORE;
     if (s.kv_dtype == PAKV_KV_BF16) {
-        if (s.head_dim == 256) hipLaunchKernelGGL(store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL(store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
+        if (s.head_dim == 256) launch(K, store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
+        else launch(K, store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
     } else {
-        if (s.head_dim == 256) hipLaunchKernelGGL(store_int8_kernel<256>, grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL(store_int8_kernel<512>, grid, dim3(256), 0, st, a);
+        if (s.head_dim == 256) launch(K, store_int8_kernel<256>, grid, dim3(256), 0, st, a);
+        else launch(K, store_int8_kernel<512>, grid, dim3(256), 0, st, a);
     }
     return (int)hipGetLastError();
 }

@@ -14,6 +14,14 @@ namespace pakv {
 
 static thread_local std::string g_last_error;
 
+struct TimingHook {
+    void* const* events = nullptr;
+    int32_t pairs = 0;
+    int32_t used = 0;
+    int32_t mask = 0;
+};
+static thread_local TimingHook g_timing;
+
 pakv_status fail(pakv_status code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -26,38 +34,30 @@ pakv_status fail(pakv_status code, const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
-// Tokens per split.  Longer contexts take longer splits so that the partial
-// results stay a few percent of the KV bytes; every split is a whole number of
-// 64-token steps (4 waves x one 16-token page each).
-DecodePlan plan_decode(const pakv_layer_desc& d, int32_t max_kv_len) {
+int timing_slot(int kind) {
+    if (!g_timing.events || !(g_timing.mask & kind) || g_timing.used >= g_timing.pairs) return -1;
+    return g_timing.used++;
+}
+
+void* const* timing_events() { return g_timing.events; }
+
+DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs) {
     DecodePlan p{};
-    int64_t span = max_kv_len;
-    if (d.window > 0 && d.window < span) span = d.window;
-    int32_t s = 128;
-    if (span > 2048) s = 256;
-    if (span > 8192) s = 512;
-    if (span > 32768) s = 1024;
-    p.split_tokens = s;
-    // Splits are aligned to multiples of S in absolute positions, so a window
-    // of W positions can touch ceil((W + S - 1) / S) of them.
-    int64_t reach = (d.window > 0) ? (int64_t)d.window + s - 1 : (int64_t)max_kv_len;
-    if (reach > max_kv_len) reach = max_kv_len;
-    int64_t n = (reach + s - 1) / s;
-    if (d.window > 0) {
-        int64_t full_n = ((int64_t)max_kv_len + s - 1) / s;
-        if (n > full_n) n = full_n;
-    }
-    p.max_splits = (int32_t)(n < 1 ? 1 : n);
+    p.grid = kDecodeGrid;
+    p.units = num_seqs * d.num_kv_heads;
     p.group = d.num_q_heads / d.num_kv_heads;
     return p;
 }
 
-size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len) {
-    DecodePlan p = plan_decode(d, max_kv_len);
-    size_t units = (size_t)num_seqs * d.num_kv_heads * p.max_splits * p.group;
-    size_t o = units * d.head_dim * sizeof(float);
-    o = (o + 255) & ~(size_t)255;
-    return o + units * 2 * sizeof(float);
+// Workspace: per-unit arrival counters, then partial o, then partial (m, l);
+// 256-byte aligned parts.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs) {
+    DecodePlan p = plan_decode(d, num_seqs);
+    size_t slots = (size_t)(p.grid + p.units) * p.group;
+    return align256((size_t)p.units * sizeof(uint32_t)) + align256(slots * d.head_dim * sizeof(float)) +
+           slots * 2 * sizeof(float);
 }
 
 static bool layer_ok(const pakv_layer_map* m, int32_t layer) {
@@ -71,6 +71,18 @@ using namespace pakv;
 extern "C" {
 
 const char* pakv_last_error(void) { return g_last_error.c_str(); }
+
+pakv_status pakv_set_timing_events(void* const* events, int32_t n_pairs, int32_t kernel_mask) {
+    clear_error();
+    if (events && n_pairs < 0) return fail(PAKV_ERR_INVALID, "n_pairs < 0");
+    g_timing.events = events;
+    g_timing.pairs = events ? n_pairs : 0;
+    g_timing.used = 0;
+    g_timing.mask = kernel_mask;
+    return PAKV_OK;
+}
+
+int32_t pakv_timing_pairs_used(void) { return g_timing.used; }
 
 pakv_status pakv_resolve_kv_sources(int32_t n_layers, const int32_t* layer_type,
                                     int32_t first_shared, int32_t* out_source) {
@@ -256,7 +268,7 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
 size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
                                    int32_t num_seqs, int32_t max_kv_len) {
     if (!layer_ok(map, layer) || num_seqs < 0 || max_kv_len < 1) return 0;
-    return decode_workspace_bytes(map->layers[layer].desc, num_seqs, max_kv_len);
+    return decode_workspace_bytes(map->layers[layer].desc, num_seqs);
 }
 
 pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
@@ -276,7 +288,10 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     const auto& L = map->layers[layer];
     const auto& S = map->layers[L.source];
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
-    size_t need = decode_workspace_bytes(L.desc, num_seqs, max_kv_len);
+    if ((int64_t)num_seqs * L.desc.num_kv_heads > kDecodeMaxUnits)
+        return fail(PAKV_ERR_UNSUPPORTED, "num_seqs * Hkv = %lld above %d per decode call",
+                    (long long)num_seqs * L.desc.num_kv_heads, kDecodeMaxUnits);
+    size_t need = decode_workspace_bytes(L.desc, num_seqs);
     if (!workspace || workspace_bytes < need)
         return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -295,11 +310,14 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     a.window = L.desc.window;
     a.kv_dtype = L.desc.kv_dtype;
     a.sm_scale = L.desc.sm_scale;
-    a.plan = plan_decode(L.desc, max_kv_len);
-    size_t units = (size_t)num_seqs * a.hkv * a.plan.max_splits * a.plan.group;
-    size_t o_bytes = (units * a.head_dim * sizeof(float) + 255) & ~(size_t)255;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    a.plan = plan_decode(L.desc, num_seqs);
+    size_t slots = (size_t)(a.plan.grid + a.plan.units) * a.plan.group;
+    char* ws = static_cast<char*>(workspace);
+    a.arrivals = reinterpret_cast<uint32_t*>(ws);
+    ws += align256((size_t)a.plan.units * sizeof(uint32_t));
+    a.part_o = reinterpret_cast<float*>(ws);
+    ws += align256(slots * a.head_dim * sizeof(float));
+    a.part_ml = reinterpret_cast<float*>(ws);
     return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
 }
 

@@ -23,14 +23,18 @@ namespace pakv {
 pakv_status fail(pakv_status code, const char* fmt, ...);
 void clear_error();
 
-// ---- decode split plan: a pure function of (layer desc, max_kv_len) --------
+// ---- decode plan -------------------------------------------------------------
+// Pass 1 runs a fixed grid of persistent workgroups (two per CU on a 256-CU
+// part); the partition of the chunk stream depends only on the lengths.
+constexpr int32_t kDecodeGrid = 512;
+constexpr int32_t kDecodeMaxUnits = 2048;    // num_seqs * Hkv per call
 struct DecodePlan {
-    int32_t split_tokens;   // S: tokens per split (multiple of 64)
-    int32_t max_splits;     // grid extent over splits
+    int32_t grid;           // workgroups of pass 1
+    int32_t units;          // num_seqs * Hkv
     int32_t group;          // Hq / Hkv
 };
-DecodePlan plan_decode(const pakv_layer_desc& d, int32_t max_kv_len);
-size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len);
+DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs);
 
 // ---- launchers (defined in the .hip translation units) ----------------------
 struct SlabView {
@@ -73,8 +77,9 @@ struct DecodeLaunch {
     int32_t kv_dtype;
     float sm_scale;
     DecodePlan plan;
-    float* part_o;    // [B][Hkv][max_splits][G][D]
-    float* part_ml;   // [B][Hkv][max_splits][G][2]
+    uint32_t* arrivals; // [units], zero between calls
+    float* part_o;      // [grid + units][G][D]
+    float* part_ml;     // [grid + units][G][2]
 };
 int launch_decode(const DecodeLaunch& a, void* stream);
 
@@ -99,5 +104,10 @@ struct ExtendLaunch {
 int launch_extend(const ExtendLaunch& a, void* stream);
 
 const char* hip_error_string(int err);
+
+// Timing hook (pakv_set_timing_events): the next event-pair index for a kernel
+// selected by `kind` (a PAKV_TIME_* bit), or -1; and the caller's event array.
+int timing_slot(int kind);
+void* const* timing_events();
 
 }  // namespace pakv

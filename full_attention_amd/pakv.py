@@ -30,8 +30,10 @@ EXPORTED = (
     "pakv_last_error", "pakv_resolve_kv_sources", "pakv_layer_map_create", "pakv_layer_map_destroy",
     "pakv_layer_map_bind_slab", "pakv_layer_map_source", "pakv_kv_bytes_per_token", "pakv_slab_bytes",
     "pakv_paged_kv_store", "pakv_decode_workspace_bytes", "pakv_paged_attn_decode",
-    "pakv_paged_attn_extend",
+    "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used",
 )
+
+TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
 
 
 class LayerDesc(ctypes.Structure):
@@ -80,6 +82,10 @@ lib.pakv_paged_attn_decode.restype = _I
 lib.pakv_paged_attn_decode.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _I, _I, _P, _S, _P]
 lib.pakv_paged_attn_extend.restype = _I
 lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
+lib.pakv_set_timing_events.restype = _I
+lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
+lib.pakv_timing_pairs_used.restype = _I
+lib.pakv_timing_pairs_used.argtypes = []
 
 
 class PakvError(RuntimeError):
@@ -196,3 +202,14 @@ def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_se
     return _check(lib.pakv_paged_attn_extend(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                              _ptr(prefix_lens), _ptr(q), _ptr(out), num_seqs, total_q,
                                              max_q_len, max_kv_len, _stream(stream)))
+
+
+def set_timing_events(events, kernel_mask):
+    """events: ctypes array of 2*n hipEvent_t handles (or None to clear)."""
+    if events is None:
+        return _check(lib.pakv_set_timing_events(None, 0, 0))
+    return _check(lib.pakv_set_timing_events(ctypes.cast(events, _P), len(events) // 2, kernel_mask))
+
+
+def timing_pairs_used():
+    return lib.pakv_timing_pairs_used()

@@ -188,13 +188,19 @@ size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
  *                 The query sits at position kv_lens[b] - 1; its own K/V must
  *                 already be stored (by this layer's source for a shared layer).
  *   q, out      : device bf16 [num_seqs][Hq][D]
- *   max_kv_len  : host upper bound on kv_lens, used to size the grid
- *   workspace   : device memory of at least pakv_decode_workspace_bytes(...)
+ *   max_kv_len  : host upper bound on kv_lens (lengths above it are clamped)
+ *   workspace   : device memory of at least pakv_decode_workspace_bytes(...),
+ *                 zero-filled before its first use; every call leaves it
+ *                 zero-filled again (per-sequence arrival counters live there).
+ *                 Calls that may overlap need separate workspaces.
+ * num_seqs * Hkv must not exceed 2048 (PAKV_ERR_UNSUPPORTED).
  * A shared layer reads its source's slab (and scales) with its own descriptor
- * (window, sm_scale, Hq).  The work of a sequence is cut into splits whose
- * boundaries depend only on the layer, max_kv_len and the sequence's own
- * length; partial results are merged in a fixed order, so the output is
- * bit-identical from run to run and does not depend on page placement. */
+ * (window, sm_scale, Hq).  The keys of all sequences form one stream of
+ * 16-token pages that a fixed number of workgroups split evenly; partial
+ * results are merged in a fixed order, so the output is bit-identical from
+ * run to run and does not depend on page placement (it may differ in the last
+ * bits when other sequences of the batch change, since they move the split
+ * points). */
 pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                    const int32_t* kv_lens, const void* q, void* out,
                                    int32_t num_seqs, int32_t max_kv_len,
@@ -216,6 +222,21 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
                                    const void* q, void* out,
                                    int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                    int32_t max_kv_len, void* stream);
+
+/* Kernel timing hook, for benchmarks and profilers.  events points to 2 *
+ * n_pairs hipEvent_t handles (caller-owned, created in the HIP runtime the
+ * library runs in); while the hook is set, each store / decode / extend call
+ * on the calling thread whose kernel is selected by kernel_mask records
+ * events[2*i] on its stream just before that kernel's launch and
+ * events[2*i + 1] just after it, for i = 0, 1, ... until the n_pairs pairs
+ * are used.  events == NULL clears the hook.  The hook adds no
+ * synchronisation; elapsed times are read by the caller (hipEventElapsedTime). */
+#define PAKV_TIME_STORE 1           /* the store kernel */
+#define PAKV_TIME_DECODE 2          /* the decode kernel */
+#define PAKV_TIME_EXTEND 8          /* the extend kernel */
+pakv_status pakv_set_timing_events(void* const* events, int32_t n_pairs, int32_t kernel_mask);
+/* Number of event pairs recorded on this thread since the hook was last set. */
+int32_t pakv_timing_pairs_used(void);
 
 #ifdef __cplusplus
 }

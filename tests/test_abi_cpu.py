@@ -181,13 +181,21 @@ def test_unbound_source_slab_is_an_error():
     assert st == pakv.ERR_INVALID and "not bound" in pakv.last_error()
 
 
-def test_workspace_grows_with_splits():
+def test_workspace_depends_on_batch_not_context():
     m = pakv.LayerMap([_desc(d=512), _desc(d=256, w=512)])
     a = pakv.decode_workspace_bytes(m, 0, 64, 4097)
-    b = pakv.decode_workspace_bytes(m, 0, 64, 131073)
-    assert 0 < a < b
-    # a sliding layer's split count is bounded by its window, not the context
-    assert pakv.decode_workspace_bytes(m, 1, 8, 131073) == pakv.decode_workspace_bytes(m, 1, 8, 4097)
+    assert a == pakv.decode_workspace_bytes(m, 0, 64, 131073)
+    assert 0 < pakv.decode_workspace_bytes(m, 0, 8, 4097) < a
+    assert pakv.decode_workspace_bytes(m, 1, 64, 4097) < a     # D 256 partials are half the size
+
+
+def test_too_many_units_per_decode_call_is_refused():
+    m = pakv.LayerMap([_desc(hq=16, hkv=8)])
+    m.bind_slab(0, 0x1000, 0x2000, 8)
+    pages = pakv.Pages(0x5000, 300, 4)
+    st = pakv.lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 300, 40,
+                                         0x8000, 1 << 30, None)
+    assert st == pakv.ERR_UNSUPPORTED
 
 
 def test_one_hip_runtime_per_process():
