@@ -60,20 +60,6 @@ def parse():
 
 # ------------------------------------------------------------------ helpers
 
-class DeviceDraws:
-    """Seeded N(0, 1) draws rounded to bf16 on the device (torch generator)."""
-
-    def __init__(self, torch, seed):
-        self.torch = torch
-        self.gen = torch.Generator(device="cuda")
-        self.gen.manual_seed(seed)
-
-    def bf16(self, shape):
-        t = self.torch
-        x = t.randn(shape, generator=self.gen, device="cuda", dtype=t.float32)
-        return x.to(t.bfloat16).view(t.int16)
-
-
 def i32(torch, x):
     return torch.tensor(np.asarray(x, dtype=np.int32), dtype=torch.int32, device="cuda")
 
@@ -130,7 +116,7 @@ class Timing:
 
 def setup_decode(torch):
     from full_attention_amd.cache import PagedKVCache
-    from workloads import e2b_decode_workload, make_page_pool
+    from workloads import DeviceDraws, e2b_decode_workload, make_page_pool
 
     wl = e2b_decode_workload()
     B = wl.num_seqs
@@ -140,7 +126,7 @@ def setup_decode(torch):
     pool = make_page_pool(rng, kv_len)
     cache = PagedKVCache(wl.layers, wl.first_shared, pool.num_pages, sentinel=True)
     cache.set_page_table(pool.page_table)
-    draws = DeviceDraws(torch, wl.seed)
+    draws = DeviceDraws(wl.seed)
     layers = wl.layers
     owners = [l for l in range(len(layers)) if cache.sources[l] == l]
     # cached rows: full layers hold every position; sliding layers only the
@@ -196,7 +182,7 @@ def decode_bytes(st):
 
 def setup_extend(torch):
     from full_attention_amd.cache import PagedKVCache
-    from workloads import e2b_extend_workload, make_page_pool
+    from workloads import DeviceDraws, e2b_extend_workload, make_page_pool
 
     wl = e2b_extend_workload()
     P = np.array(wl.cached_lens, dtype=np.int64)
@@ -206,7 +192,7 @@ def setup_extend(torch):
     pool = make_page_pool(rng, P + n)
     cache = PagedKVCache(wl.layers, wl.first_shared, pool.num_pages, sentinel=True)
     cache.set_page_table(pool.page_table)
-    draws = DeviceDraws(torch, wl.seed)
+    draws = DeviceDraws(wl.seed)
     layers = wl.layers
     owners = [l for l in range(len(layers)) if cache.sources[l] == l]
     cu_n = np.concatenate([[0], np.cumsum(n)])

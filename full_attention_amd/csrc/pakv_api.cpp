@@ -49,14 +49,15 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs) {
     return p;
 }
 
-// Workspace: per-unit arrival counters, then partial o, then partial (m, l);
-// 256-byte aligned parts.
+// Workspace: arrival counters (a fixed region of kDecodeMaxUnits, so that
+// layers of any shape can share one workspace and leave it zeroed), then
+// partial o, then partial (m, l); 256-byte aligned parts.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs) {
     DecodePlan p = plan_decode(d, num_seqs);
     size_t slots = (size_t)(p.grid + p.units) * p.group;
-    return align256((size_t)p.units * sizeof(uint32_t)) + align256(slots * d.head_dim * sizeof(float)) +
+    return align256((size_t)kDecodeMaxUnits * sizeof(uint32_t)) + align256(slots * d.head_dim * sizeof(float)) +
            slots * 2 * sizeof(float);
 }
 
@@ -314,7 +315,7 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     size_t slots = (size_t)(a.plan.grid + a.plan.units) * a.plan.group;
     char* ws = static_cast<char*>(workspace);
     a.arrivals = reinterpret_cast<uint32_t*>(ws);
-    ws += align256((size_t)a.plan.units * sizeof(uint32_t));
+    ws += align256((size_t)kDecodeMaxUnits * sizeof(uint32_t));
     a.part_o = reinterpret_cast<float*>(ws);
     ws += align256(slots * a.head_dim * sizeof(float));
     a.part_ml = reinterpret_cast<float*>(ws);

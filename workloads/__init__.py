@@ -16,7 +16,10 @@ from .configs import (
     WORKLOADS,
 )
 
+from .device import DeviceDraws
+
 __all__ = [
+    "DeviceDraws",
     "PAGE_SIZE", "bf16_from_f32", "bf16_to_f32", "normal_bf16", "rms_normalise_bf16",
     "PagePool", "make_page_pool",
     "LayerSpec", "Workload", "tiny_workload", "e2b_decode_workload", "e2b_extend_workload",
