@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of a graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -73,19 +76,19 @@ def source_hash(*names):
 
 
 def load_traffic(kernel, workload, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_e2b_step_traffic.md")
     if not os.path.exists(path):
         return None
-    try:
-        data = json.load(open(path))
-    except ValueError:
-        return None
-    rec = data.get(f"{kernel}|{workload}")
-    if not rec or rec.get("source_hash") != src_hash:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for line in open(path):
+        if not line.startswith("traffic-record "):
+            continue
+        fields = dict(re.findall(r"(\w+)=(.*?)(?= \w+=|$)", line.strip()[len("traffic-record "):]))
+        if (fields.get("kernel") == kernel and fields.get("workload") == workload
+                and fields.get("source_hash") == src_hash):
+            return int(fields["hbm_bytes_per_launch"])
+    return None
 
 
 class Timing:
@@ -344,6 +347,13 @@ def main():
     from full_attention_amd import pakv
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     st = setup_decode(torch)
     nl = len(st["layers"])
     ms_step, graph = run_graph_or_eager(torch, lambda: decode_step(st), args.steps, args.warmup, args.eager)
