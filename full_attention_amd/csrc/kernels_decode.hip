@@ -127,41 +127,77 @@ struct Cfg {
     static constexpr int KV_DMA = 2 * PAGE / (1024 * kWaves);   // copies per wave per chunk
     static constexpr int PER = KV_DMA + (INT8 ? 1 : 0);
     static constexpr int SX = kWaves * 64 * 16;             // partial-score exchange
-    static constexpr int OFF = ((pakv::kDecodeMaxUnits + 1) * 4 + 15) & ~15;
-    static constexpr int LDS = NBUF * BUF + SX + OFF;
+    static constexpr int SEQ = (2 * (pakv::kDecodeMaxSeqs + 1) * 4 + 15) & ~15;   // per-sequence table
+    static constexpr int LDS = NBUF * BUF + SX + SEQ;
     static constexpr int KK = D / 128;                      // 32-dim steps in a wave's quarter
     static constexpr int MT = D / 64;                       // 16-dim output tiles in a quarter
     static_assert(LDS <= 80 * 1024, "two workgroups per CU");
 };
 
-// Chunks of a unit: pages from lo/16 to (L-1)/16.
-struct Unit {
-    int32_t u, b, g, lo, hi, page0, n;
+// Per-sequence table in LDS, built once per workgroup from kv_lens:
+//   soff[b] = first chunk of sequence b's units (units of a sequence are
+//             consecutive, one per KV head, each n_b chunks), soff[B] = total
+//   slen[b] = clamped length of sequence b
+struct SeqTable {
+    int32_t* soff;   // [B + 1]
+    int32_t* slen;   // [B]
 };
 
-__device__ __forceinline__ Unit make_unit(const DecodeArgs& a, const int32_t* __restrict__ kv_lens, int32_t u) {
+// Chunks of a unit: pages from lo/16 to (L-1)/16.
+struct Unit {
+    int32_t u, b, g, lo, hi, page0, n, first;   // first = stream index of its chunk 0
+};
+
+__device__ __forceinline__ int32_t window_lo(const DecodeArgs& a, int32_t len) {
+    return (a.window > 0 && len > a.window) ? len - a.window : 0;
+}
+
+__device__ __forceinline__ int32_t chunks_of(const DecodeArgs& a, int32_t len) {
+    return ((len + 15) >> 4) - (window_lo(a, len) >> 4);
+}
+
+__device__ __forceinline__ Unit unit_of(const DecodeArgs& a, const SeqTable& st, int32_t u) {
     Unit x;
     x.u = u;
     x.b = u / a.hkv;
     x.g = u - x.b * a.hkv;
-    const int32_t len = clamp_i32(kv_lens[x.b], 1, a.max_kv_len);
-    x.hi = len;
-    x.lo = (a.window > 0 && len > a.window) ? len - a.window : 0;
+    x.hi = st.slen[x.b];
+    x.lo = window_lo(a, x.hi);
     x.page0 = x.lo >> 4;
-    x.n = ((len + 15) >> 4) - x.page0;
+    x.n = ((x.hi + 15) >> 4) - x.page0;
+    x.first = st.soff[x.b] + x.g * x.n;
     return x;
 }
 
-// off[u] = first chunk of unit u in the stream, off[U] = total (block-wide scan).
-__device__ __forceinline__ void build_offsets(const DecodeArgs& a, const int32_t* __restrict__ kv_lens,
-                                              int32_t* off, int32_t U) {
+// Sequence holding stream chunk c: the last b with soff[b] <= c.
+__device__ __forceinline__ int32_t seq_of_chunk(const SeqTable& st, int32_t B, int32_t c) {
+    int32_t lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (st.soff[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void advance(const DecodeArgs& a, const SeqTable& st, int32_t U, Unit& x, int32_t& k) {
+    if (++k == x.n && x.u + 1 < U) {
+        x = unit_of(a, st, x.u + 1);
+        k = 0;
+    }
+}
+
+__device__ __forceinline__ void build_seq_table(const DecodeArgs& a, const int32_t* __restrict__ kv_lens,
+                                                const SeqTable& st, int32_t B) {
     __shared__ int32_t wave_tot[kWaves];
     const int t = threadIdx.x;
-    const int per_t = (U + 255) / 256;
-    const int u0 = t * per_t, u1 = min(u0 + per_t, U);
+    const int per_t = (B + 255) / 256;
+    const int b0 = t * per_t, b1 = min(b0 + per_t, B);
     int32_t local = 0;
-    for (int u = u0; u < u1; ++u) local += make_unit(a, kv_lens, u).n;
-    // inclusive scan of `local` across the block
+    for (int b = b0; b < b1; ++b) {
+        const int32_t len = clamp_i32(kv_lens[b], 1, a.max_kv_len);
+        st.slen[b] = len;
+        local += chunks_of(a, len) * a.hkv;
+    }
     int32_t incl = local;
     const int lane = t & 63, wave = t >> 6;
 #pragma unroll
@@ -173,21 +209,49 @@ __device__ __forceinline__ void build_offsets(const DecodeArgs& a, const int32_t
     __syncthreads();
     int32_t before = 0;
     for (int w = 0; w < wave; ++w) before += wave_tot[w];
-    int32_t run = before + incl - local;     // exclusive prefix of this thread's units
-    for (int u = u0; u < u1; ++u) {
-        off[u] = run;
-        run += make_unit(a, kv_lens, u).n;
+    int32_t run = before + incl - local;
+    for (int b = b0; b < b1; ++b) {
+        st.soff[b] = run;
+        run += chunks_of(a, st.slen[b]) * a.hkv;
     }
-    if (t == 255) off[U] = before + incl;
+    if (t == 255) st.soff[B] = before + incl;
     __syncthreads();
 }
 
+// Page ids of stream chunks c0 .. c0 + 63 (lane j holds chunk c0 + j; lanes
+// past `count` hold 0).  Ids outside the pool become 0, so a bad table never
+// makes a copy leave the slab.
+__device__ __forceinline__ uint32_t load_ids(const DecodeArgs& a, const int32_t* __restrict__ page_table,
+                                             const SeqTable& st, int32_t B, int32_t c0, int32_t count, int lane) {
+    uint32_t id = 0;
+    if (lane < count) {
+        const int32_t c = c0 + lane;
+        const int32_t b = seq_of_chunk(st, B, c);
+        const int32_t len = st.slen[b];
+        const int32_t n = chunks_of(a, len);
+        const int32_t k = (c - st.soff[b]) % n;
+        const int32_t ph = page_table[(int64_t)b * a.max_pages + (window_lo(a, len) >> 4) + k];
+        id = ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : 0u;
+    }
+    return id;
+}
+
+// Q^T operand of a wave's dim quarter: column `col` = head g*G + col (zero
+// for padding columns), dims dq + 32*kk + 8*qg .. +8.
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, const Unit& x, int32_t G, int col, int qg, int dq,
+                                       u32x4 (&qreg)[D / 128]) {
+    const bool real = col < G;
+    const uint16_t* qp = a.q + ((int64_t)x.b * a.hq + (int64_t)x.g * G + (real ? col : 0)) * D + dq + 8 * qg;
+#pragma unroll
+    for (int kk = 0; kk < D / 128; ++kk)
+        qreg[kk] = real ? *reinterpret_cast<const u32x4*>(qp + 32 * kk) : u32x4{0, 0, 0, 0};
+}
+
 template <int D, bool INT8>
-__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, const int32_t* __restrict__ page_table,
-                                            uint8_t* buf, const Unit& x, int32_t k, int wave, int lane) {
+__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, uint8_t* buf, const Unit& x,
+                                            int wave, int lane) {
     using C = Cfg<D, INT8>;
-    int32_t phys = page_table[(int64_t)x.b * a.max_pages + x.page0 + k];
-    phys = ((uint32_t)phys < (uint32_t)a.num_pages) ? phys : 0;   // out-of-pool ids never fault
     const int64_t blk = ((int64_t)phys * a.hkv + x.g) * C::PAGE;
     const uint8_t* kp = a.k_slab + blk;
     const uint8_t* vp = a.v_slab + blk;
@@ -215,18 +279,6 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, const int32_t* 
             dma16(src, vb + C::PAGE + wave * 32);
         }
     }
-}
-
-// Q^T operand of a wave's dim quarter: column `col` = head g*G + col (zero
-// for padding columns), dims dq + 32*kk + 8*qg .. +8.
-template <int D>
-__device__ __forceinline__ void load_q(const DecodeArgs& a, const Unit& x, int32_t G, int col, int qg, int dq,
-                                       u32x4 (&qreg)[D / 128]) {
-    const bool real = col < G;
-    const uint16_t* qp = a.q + ((int64_t)x.b * a.hq + (int64_t)x.g * G + (real ? col : 0)) * D + dq + 8 * qg;
-#pragma unroll
-    for (int kk = 0; kk < D / 128; ++kk)
-        qreg[kk] = real ? *reinterpret_cast<const u32x4*>(qp + 32 * kk) : u32x4{0, 0, 0, 0};
 }
 
 // Partials cross workgroups (and XCDs, whose L2s are not coherent with each
@@ -269,124 +321,157 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 }
 
 // Merges the partials of unit x (slots w + x.u for w in [w0, w1], in that
-// order) and writes the G heads' bf16 outputs.  64 threads per head, each
-// owning D/64 dims; partials are read 8 slots per batch.
+// order) and writes the G heads' bf16 outputs.  A thread owns up to two
+// (head, 4-dim) items per pass and reads 8 slots per batch, so a unit of up
+// to 8 partials with G * D <= 2048 is merged in one round trip.
 template <int D>
 __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
-    constexpr int DPT = D / 64;
-    constexpr int NV = DPT / 4;
     constexpr int BATCH = 8;
-    for (int hl = t >> 6; hl < G; hl += kWaves) {
-        const int d0 = (t & 63) * DPT;
-        // running max and rescaled sums over batches, in slot order
-        float M = -INFINITY, L = 0.f;
-        f32x4 acc[NV];
+    const int n_items = G * (D / 4);
+    for (int base = 0; base < n_items; base += 512) {
+        int hl[2], d0[2];
+        bool on[2];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 2; ++i) {
+            const int it = base + i * 256 + t;
+            on[i] = it < n_items;
+            hl[i] = on[i] ? it / (D / 4) : 0;
+            d0[i] = on[i] ? (it % (D / 4)) * 4 : 0;
+        }
+        float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         for (int32_t wb = w0; wb <= w1; wb += BATCH) {
-            f32x2 ml[BATCH];
-            f32x4 ov[BATCH * NV];
+            f32x2 ml[2 * BATCH];
+            f32x4 ov[2 * BATCH];
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int32_t w = min(wb + k, w1);
-                const int64_t sl = ((int64_t)w + x.u) * G + hl;
-                ml[k] = get2(a.part_ml + sl * 2);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) ov[k * NV + v] = get4(a.part_o + sl * D + d0 + 4 * v);
+                for (int i = 0; i < 2; ++i) {
+                    if (on[i]) {
+                        const int64_t sl = ((int64_t)w + x.u) * G + hl[i];
+                        ml[i * BATCH + k] = get2(a.part_ml + sl * 2);
+                        ov[i * BATCH + k] = get4(a.part_o + sl * D + d0[i]);
+                    }
+                }
             }
             await(ml);
             await(ov);
-            float Mb = M;
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k)
-                if (wb + k <= w1) Mb = fmaxf(Mb, ml[k].x);
-            const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
-            const float r = exp2f(M - Mb_use);         // rescale what came before
-            L *= r;
+            for (int i = 0; i < 2; ++i) {
+                float Mb = M[i];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) acc[v] *= r;
+                for (int k = 0; k < BATCH; ++k)
+                    if (wb + k <= w1) Mb = fmaxf(Mb, ml[i * BATCH + k].x);
+                const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
+                const float r = exp2f(M[i] - Mb_use);        // rescale what came before
+                L[i] *= r;
+                acc[i] *= r;
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k) {
-                if (wb + k > w1) break;
-                const float wt = exp2f(ml[k].x - Mb_use);
-                L += wt * ml[k].y;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) acc[v] += wt * ov[k * NV + v];
+                for (int k = 0; k < BATCH; ++k) {
+                    if (wb + k > w1) break;
+                    const float wt = exp2f(ml[i * BATCH + k].x - Mb_use);
+                    L[i] += wt * ml[i * BATCH + k].y;
+                    acc[i] += wt * ov[i * BATCH + k];
+                }
+                M[i] = Mb;
             }
-            M = Mb;
         }
-        const float inv = 1.0f / L;
-        uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl) * D + d0;
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-            *reinterpret_cast<u32x2*>(op + 4 * v) =
-                u32x2{pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv), pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv)};
+        for (int i = 0; i < 2; ++i) {
+            if (!on[i]) continue;
+            const float inv = 1.0f / L[i];
+            uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl[i]) * D + d0[i];
+            *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv),
+                                                  pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv)};
+        }
     }
 }
 
 template <int D, bool INT8>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
-                                                                 const int32_t* __restrict__ kv_lens) {
+                                                         const int32_t* __restrict__ kv_lens) {
     using C = Cfg<D, INT8>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
-    int32_t* off = reinterpret_cast<int32_t*>(lds + C::NBUF * C::BUF + C::SX);
     __shared__ uint32_t ticket;
     f32x4* sx = reinterpret_cast<f32x4*>(lds + C::NBUF * C::BUF);
+    int32_t* seq_lds = reinterpret_cast<int32_t*>(lds + C::NBUF * C::BUF + C::SX);
+    const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int qg = lane >> 4;            // 4-row group of the MFMA layouts
     const int col = lane & 15;           // head column
     const int32_t G = a.group;
-    const int32_t U = a.num_seqs * a.hkv;
+    const int32_t B = a.num_seqs;
+    const int32_t U = B * a.hkv;
 
-    build_offsets(a, kv_lens, off, U);
-    const int32_t T = off[U];
+    build_seq_table(a, kv_lens, st, B);
+    const int32_t T = st.soff[B];
     const int32_t per = (T + a.grid - 1) / a.grid;
     const int32_t c_begin = blockIdx.x * per;
     const int32_t c_end = min(c_begin + per, T);
     if (c_begin >= c_end) return;
     const int32_t total = c_end - c_begin;
 
-    // unit holding c_begin: last u with off[u] <= c_begin
-    int32_t lo_u = 0, hi_u = U - 1;
-    while (lo_u < hi_u) {
-        const int32_t mid = (lo_u + hi_u + 1) >> 1;
-        if (off[mid] <= c_begin) lo_u = mid; else hi_u = mid - 1;
+    // first unit of the run, and the page ids of its first 64 chunks (with Q:
+    // one round trip before the first copy)
+    Unit uc;
+    int32_t kc;
+    {
+        const int32_t b = seq_of_chunk(st, B, c_begin);
+        const int32_t n = chunks_of(a, st.slen[b]);
+        const int32_t r = c_begin - st.soff[b];
+        uc = unit_of(a, st, b * a.hkv + r / n);
+        kc = r % n;
     }
-    Unit ui = make_unit(a, kv_lens, lo_u);        // issue cursor
-    int32_t ki = c_begin - off[lo_u];
-    Unit uc = ui;                                 // compute cursor
-    int32_t kc = ki;
-
+    Unit ui = uc;                                 // issue cursor
+    int32_t ki = kc;
+    uint32_t ids = load_ids(a, page_table, st, B, c_begin, min(total, 64), lane);
     const int dq = wave * (D / 4);
     u32x4 qreg[C::KK];
     load_q<D>(a, uc, G, col, qg, dq, qreg);
-    wait_vm<0>();   // Q has landed; nothing the compiler issued stays in flight under the copies
+    wait_vm<0>();   // ids and Q have landed; nothing the compiler issued stays in flight
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
-            issue_chunk<D, INT8>(a, page_table, lds + c * C::BUF, ui, ki, wave, lane);
-            if (++ki == ui.n && ui.u + 1 < U) { ui = make_unit(a, kv_lens, ui.u + 1); ki = 0; }
+            issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui, wave, lane);
+            advance(a, st, U, ui, ki);
         }
     }
 
     f32x4 o[C::MT];
+#pragma unroll
+    for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
     for (int32_t i = 0; i < total; ++i) {
         wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
         lds_barrier();
         if (kc == 0 || i == 0) {
-            // a new unit inside the run: its Q (this load drains the copies in flight)
-            if (i > 0) load_q<D>(a, uc, G, col, qg, dq, qreg);
+            // a new unit inside the run: its Q.  The wait drains the copies in
+            // flight, but only here: with no load left pending across the
+            // loop's back edge, the compiler has no reason to wait on the
+            // (in-order) vector-memory counter anywhere else in the loop.
+            if (i > 0) {
+                load_q<D>(a, uc, G, col, qg, dq, qreg);
+                wait_vm<0>();
+            }
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
             m_run = -INFINITY;
             l_run = 0.0f;
         }
-        if (i + C::NBUF - 1 < total) {
-            issue_chunk<D, INT8>(a, page_table, lds + ((i + C::NBUF - 1) % C::NBUF) * C::BUF, ui, ki, wave, lane);
-            if (++ki == ui.n && ui.u + 1 < U) { ui = make_unit(a, kv_lens, ui.u + 1); ki = 0; }
+        {
+            const int32_t j = i + C::NBUF - 1;        // chunk to copy now
+            if (j < total) {
+                if ((j & 63) == 0) {                  // next window of page ids (drains, once per 64)
+                    ids = load_ids(a, page_table, st, B, c_begin + j, min(total - j, 64), lane);
+                    wait_vm<0>();
+                }
+                issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, j & 63),
+                                     lds + (j % C::NBUF) * C::BUF, ui, wave, lane);
+                advance(a, st, U, ui, ki);
+            }
         }
         const uint8_t* kbuf = lds + (i % C::NBUF) * C::BUF;
         const uint8_t* vbuf = kbuf + C::PAGE;
@@ -483,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
         // ---- end of this run's part of the unit --------------------------------
         if (kc == uc.n - 1 || i == total - 1) {
             const float l_tot = wave_sum_across_groups(l_run);
-            const int32_t w0 = off[uc.u] / per, w1 = (off[uc.u + 1] - 1) / per;
+            const int32_t w0 = uc.first / per, w1 = (uc.first + uc.n - 1) / per;
             if (w0 == w1) {
                 // the whole unit is in this run: normalise and write the outputs
                 if (col < G) {
@@ -510,7 +595,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
                 }
             }
         }
-        if (++kc == uc.n && uc.u + 1 < U) { uc = make_unit(a, kv_lens, uc.u + 1); kc = 0; }
+        advance(a, st, U, uc, kc);
     }
     wait_vm<0>();
 }

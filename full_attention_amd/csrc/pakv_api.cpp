@@ -289,6 +289,8 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     const auto& L = map->layers[layer];
     const auto& S = map->layers[L.source];
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
+    if (num_seqs > kDecodeMaxSeqs)
+        return fail(PAKV_ERR_UNSUPPORTED, "num_seqs %d above %d per decode call", num_seqs, kDecodeMaxSeqs);
     if ((int64_t)num_seqs * L.desc.num_kv_heads > kDecodeMaxUnits)
         return fail(PAKV_ERR_UNSUPPORTED, "num_seqs * Hkv = %lld above %d per decode call",
                     (long long)num_seqs * L.desc.num_kv_heads, kDecodeMaxUnits);

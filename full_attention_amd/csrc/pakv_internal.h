@@ -27,7 +27,8 @@ void clear_error();
 // Pass 1 runs a fixed grid of persistent workgroups (two per CU on a 256-CU
 // part); the partition of the chunk stream depends only on the lengths.
 constexpr int32_t kDecodeGrid = 512;
-constexpr int32_t kDecodeMaxUnits = 2048;    // num_seqs * Hkv per call
+constexpr int32_t kDecodeMaxSeqs = 1023;     // sequences per decode call
+constexpr int32_t kDecodeMaxUnits = 8192;    // num_seqs * Hkv per decode call
 struct DecodePlan {
     int32_t grid;           // workgroups of pass 1
     int32_t units;          // num_seqs * Hkv

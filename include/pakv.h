@@ -193,7 +193,7 @@ size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
  *                 zero-filled before its first use; every call leaves it
  *                 zero-filled again (per-sequence arrival counters live there).
  *                 Calls that may overlap need separate workspaces.
- * num_seqs * Hkv must not exceed 2048 (PAKV_ERR_UNSUPPORTED).
+ * num_seqs must not exceed 1023 and num_seqs * Hkv 8192 (PAKV_ERR_UNSUPPORTED).
  * A shared layer reads its source's slab (and scales) with its own descriptor
  * (window, sm_scale, Hq).  The keys of all sequences form one stream of
  * 16-token pages that a fixed number of workgroups split evenly; partial

@@ -189,13 +189,14 @@ def test_workspace_depends_on_batch_not_context():
     assert pakv.decode_workspace_bytes(m, 1, 64, 4097) < a     # D 256 partials are half the size
 
 
-def test_too_many_units_per_decode_call_is_refused():
+def test_too_many_sequences_or_units_per_decode_call_are_refused():
     m = pakv.LayerMap([_desc(hq=16, hkv=8)])
     m.bind_slab(0, 0x1000, 0x2000, 8)
-    pages = pakv.Pages(0x5000, 300, 4)
-    st = pakv.lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, 300, 40,
-                                         0x8000, 1 << 30, None)
-    assert st == pakv.ERR_UNSUPPORTED
+    for nseq in (1024, 1100):
+        pages = pakv.Pages(0x5000, nseq, 4)
+        st = pakv.lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, nseq, 40,
+                                             0x8000, 1 << 30, None)
+        assert st == pakv.ERR_UNSUPPORTED, nseq
 
 
 def test_one_hip_runtime_per_process():
