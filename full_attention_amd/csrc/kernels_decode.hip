@@ -38,6 +38,7 @@
 // other keys are selected to -inf, and their value elements are selected to
 // zero before the product (slots that were never written may hold NaN).
 
+#include "async_copy.h"
 #include "device_common.h"
 #include "launch_timing.h"
 #include "pakv_internal.h"
@@ -71,31 +72,6 @@ struct DecodeArgs {
     float* part_ml;         // [grid + U][G][2]
 };
 
-// ---- asynchronous global -> LDS copies -----------------------------------
-// One instruction copies 16 bytes per active lane; lane i writes LDS byte
-// address m0 + 16*i.  M0 is saved and restored around it (the compiler keeps
-// its own values there), with the one wait state the hardware needs between
-// writing M0 and an LDS-DMA instruction.  The compiler does not track these
-// copies: completion is awaited explicitly (wait_vm) before a barrier.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gaddr)
-        : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
 // flight (newer <= NBUF - 2).
 template <int PER, int NBUF>
@@ -105,16 +81,6 @@ __device__ __forceinline__ void wait_chunks(int newer) {
     if constexpr (NBUF >= 3) { if (newer >= 1) { wait_vm<PER>(); return; } }
     wait_vm<0>();
 }
-
-// Barrier for LDS traffic only: waits for this wave's LDS reads/writes (not
-// for the global->LDS copies in flight) and orders the compiler around it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 template <int D, bool INT8>
 struct Cfg {
