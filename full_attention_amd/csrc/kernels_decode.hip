@@ -252,8 +252,17 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
 // coherence), which need no writeback or invalidation of a whole L2.  They are
 // issued in batches from inline assembly and awaited explicitly; the wait
 // takes the loaded registers as operands, so nothing reads them earlier.
+//
+// Two hazards the compiler cannot see through this asm are handled by hand:
+// - A store with more than 8 bytes of data reads its data registers after it
+//   issues, so the next instruction must not overwrite them at once; put4
+//   ends with an s_nop that keeps the next instruction out of that window.
+// - A memory instruction that reads an MFMA result needs wait states after
+//   the MFMA; mfma_settle() (24 wait states, more than any MFMA here needs)
+//   separates the value product from the put4s that store its output.
+__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 __device__ __forceinline__ void put4(float* p, f32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void put2(float* p, float x, float y) {
     asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(f32x2{x, y}) : "memory");
@@ -547,6 +556,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
                 }
             } else {
                 const int64_t slot = ((int64_t)blockIdx.x + uc.u) * G;
+                mfma_settle();
                 if (col < G) {
                     float* po = a.part_o + (slot + col) * D + dq;
 #pragma unroll

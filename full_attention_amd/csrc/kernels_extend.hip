@@ -5,7 +5,7 @@
 // flattened token-major (row r = token * G + head), so each K/V tile staged in
 // LDS serves every head of the group.  Each wavefront owns 32 rows and walks
 // the workgroup's kv range in 32-token tiles (two pages), copied global -> LDS
-// asynchronously one tile ahead:
+// asynchronously ahead of use:
 //
 //   S^T[32 kv x 32 rows] = K_tile . Q^T        D/16 MFMA 32x32x16
 //   online softmax per row in the exp2 domain; the running max is raised (and
@@ -19,8 +19,13 @@
 // never goes through LDS.  V pages are dim-major, so the value MFMA's A operand
 // (one dim, 8 consecutive tokens) is one 16-byte LDS read.
 //
-// D = 256: 8 wavefronts (256 rows) per workgroup, two per SIMD, Q^T and O^T in
-// registers.  D = 512: 4 wavefronts (128 rows), one per SIMD, O^T in 256 AGPRs.
+// Four wavefronts per workgroup, one per SIMD, each owning 512/D blocks of 32
+// rows (D = 512: one, 128 rows per workgroup; D = 256: two, 256 rows, so
+// every K or V operand read from LDS feeds two MFMAs); O^T lives in AGPRs (16
+// tiles), Q^T and the score tiles in VGPRs.  K and V have rings of
+// two tiles each, and a wavefront's step t runs the score product of tile t+1
+// and the value product of tile t interleaved (two independent MFMA chains),
+// then the softmax of tile t+1; K(t+2) and V(t+1) are copied meanwhile.
 //
 // Masks: the query row at position p sees kv position j iff j <= p and, on a
 // sliding layer, p - j < W (unsloth commit ca9dbce, one block mask per regime;
@@ -44,6 +49,7 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;            // kv tokens per staged tile (two pages)
+constexpr int kRankedSeqs = 256;     // sequences ordered by weight at dispatch (one per thread)
 constexpr float kRescale = 8.0f;     // raise the running max only past 2^8
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
@@ -69,14 +75,22 @@ __device__ __forceinline__ void asm_mfma_acc(f32x16& c, u32x4 a, u32x4 b) {
 __device__ __forceinline__ void asm_mfma_drain(f32x16& c) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
 }
+// Value MFMA with its accumulator tile held in AGPRs (the "a" constraint keeps
+// the tile there).  Its B operand (P^T) is written by the VALU shortly before
+// the first value MFMA of a step, which therefore takes the s_nop form.
+__device__ __forceinline__ void asm_mfma_agpr(f32x16& c, u32x4 a, u32x4 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void asm_mfma_agpr_nop(f32x16& c, u32x4 a, u32x4 b) {
+    asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
 
 // o *= al for an accumulator tile that lives in AGPRs, written as explicit
 // AGPR read / multiply / write so that the compiler keeps the tile in the AGPR
-// file across the loop.  Called at most a few times per workgroup; it is
-// fenced by wait states for the MFMA that last wrote the tile and for the
-// MFMA that next reads it.
+// file across the loop.  Called at most a few times per workgroup, after
+// settle_tiles() (the MFMAs that last wrote the tiles have landed); it ends
+// with the wait states the next MFMA that reads the tile needs.
 __device__ __forceinline__ void agpr_scale(f32x16& o, float al) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         float x = o[e], t;
@@ -94,6 +108,22 @@ __device__ __forceinline__ void agpr_scale(f32x16& o, float al) {
 // Pins a tile to the AGPR file at this point (no instruction is emitted), so
 // the loop-carried accumulators are not copied into VGPRs at the back edge.
 __device__ __forceinline__ void pin_agpr(f32x16& o) { asm volatile("" : "+a"(o)); }
+
+// 24 wait states that every accumulator tile passes through: the value MFMAs
+// are inline asm, so the compiler does not know that the tiles are written by
+// an MFMA still in flight, and any read it schedules (a copy, a rescale, the
+// output) must come after this statement, which takes all tiles as operands.
+#define PAKV_SETTLE "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+__device__ __forceinline__ void settle_tiles(f32x16 (&o)[8]) {
+    asm volatile(PAKV_SETTLE : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
+                 "+a"(o[7]));
+}
+__device__ __forceinline__ void settle_tiles(f32x16 (&o)[16]) {
+    asm volatile(PAKV_SETTLE : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
+                 "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
+                 "+a"(o[14]), "+a"(o[15]));
+}
+#undef PAKV_SETTLE
 
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
@@ -145,67 +175,195 @@ __device__ __forceinline__ int k_swz(int tk) { return (tk & 3) | ((tk >> 1) & 4)
 
 template <int D>
 struct XCfg {
-    static constexpr int NW = (D == 256) ? 8 : 4;       // wavefronts per workgroup
+    static constexpr int NW = 4;                        // wavefronts per workgroup, one per SIMD
     static constexpr int THREADS = 64 * NW;
-    static constexpr int ROWS = 32 * NW;                // query rows per workgroup
+    static constexpr int NRB = 512 / D;                 // 32-row blocks per wavefront (O^T fills 256 AGPRs)
+    static constexpr int ROWS = 32 * NRB * NW;          // query rows per workgroup
     static constexpr int KROW = D * 2;                  // bytes per K row
     static constexpr int PAGE = 16 * D * 2;             // bytes per (page, head) block
-    static constexpr int TILE = 4 * PAGE;               // K (2 pages) + V (2 pages)
-    static constexpr int NBUF = 2;
-    static constexpr int DMA = TILE / 1024 / NW;         // 1 KiB copies per wave per tile
-    static constexpr int LDS = NBUF * TILE;
+    static constexpr int HALF = 2 * PAGE;               // K (or V) of one 32-token tile
+    static constexpr int DMA = HALF / 1024 / NW;        // 1 KiB copies per wave per K (or V) tile
+    static constexpr int LDS = 4 * HALF;                // K ring of 2 tiles, V ring of 2 tiles
     static constexpr int KK = D / 16;                   // 16-dim steps of the score product
     static constexpr int MT = D / 32;                   // 32-dim tiles of the output
-    static_assert(DMA % 2 == 0 && DMA * NW * 1024 == TILE, "tile copies must split evenly");
+    static_assert(KK == 2 * MT, "one score MFMA per value MFMA");
+    static_assert(DMA * NW * 1024 == HALF, "tile copies must split evenly");
 };
 
-// Copies K and V of the tile whose two pages are physical pages ph0, ph1.
-// Copy `inst` of the K region fills LDS bytes [1024 inst, +1024): K rows
+// Copies the K rows of the tile whose two pages are physical pages ph0, ph1.
+// Copy `inst` fills LDS bytes [1024 inst, +1024): K rows
 // tk = inst * 64 / (D / 8) + lane / (D / 8), with granule colp ^ key(tk) of
-// row tk landing at granule colp.  Copy `inst` of the V region fills dims
-// d = 32 inst + lane / 2 (page inst / (D / 32)), half (lane & 1) ^ bit 2 of d.
+// row tk landing at granule colp.
 template <int D>
-__device__ __forceinline__ void issue_tile(const ExtendArgs& a, uint32_t kb, int32_t ph0, int32_t ph1, int32_t g,
-                                           int wave, int lane) {
+__device__ __forceinline__ void issue_k_part(const ExtendArgs& a, uint32_t kb, int32_t ph0, int32_t ph1, int32_t g,
+                                             int wave, int lane, int i) {
     using C = XCfg<D>;
     constexpr int GR = C::KROW / 16;                    // granules per K row (32 or 64)
-    const uint32_t vb = kb + 2 * C::PAGE;
-    const uint8_t* kbase[2] = {
-        reinterpret_cast<const uint8_t*>(a.k_slab) + ((int64_t)ph0 * a.hkv + g) * C::PAGE,
-        reinterpret_cast<const uint8_t*>(a.k_slab) + ((int64_t)ph1 * a.hkv + g) * C::PAGE};
-    const uint8_t* vbase[2] = {
-        reinterpret_cast<const uint8_t*>(a.v_slab) + ((int64_t)ph0 * a.hkv + g) * C::PAGE,
-        reinterpret_cast<const uint8_t*>(a.v_slab) + ((int64_t)ph1 * a.hkv + g) * C::PAGE};
+    const int inst = wave + C::NW * i;                  // wave-uniform
+    const int32_t ph = ((inst * 64) / (16 * GR)) ? ph1 : ph0;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_slab) + ((int64_t)ph * a.hkv + g) * C::PAGE;
     const int colp = lane % GR;
-    const int v_lane = (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 3) & 1)) * 16);
+    const int tk = (inst * 64 + lane) / GR;
+    const uint32_t off = (tk & 15) * C::KROW + ((colp ^ k_swz(tk)) * 16);
+    dma16_s(kbase, off, kb + inst * 1024);
+}
+template <int D>
+__device__ __forceinline__ void issue_k(const ExtendArgs& a, uint32_t kb, int32_t ph0, int32_t ph1, int32_t g,
+                                        int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < C::DMA / 2; ++i) {
-        const int inst = wave + C::NW * i;                      // wave-uniform
-        const int tk = (inst * 64 + lane) / GR;                 // uniform when GR = 64
-        const uint32_t off = (tk & 15) * C::KROW + ((colp ^ k_swz(tk)) * 16);
-        dma16_s(kbase[(inst * 64) / (16 * GR)], off, kb + inst * 1024);
+    for (int i = 0; i < XCfg<D>::DMA; ++i) issue_k_part<D>(a, kb, ph0, ph1, g, wave, lane, i);
+}
+
+// Copies the V pages of the same tile: copy `inst` fills dims
+// d = 32 inst + lane / 2 (page inst / (D / 32)), half (lane & 1) ^ bit 2 of d.
+template <int D>
+__device__ __forceinline__ void issue_v_part(const ExtendArgs& a, uint32_t vb, int32_t ph0, int32_t ph1, int32_t g,
+                                             int wave, int lane, int i) {
+    using C = XCfg<D>;
+    const int inst = wave + C::NW * i;
+    const int32_t ph = (inst / (D / 32)) ? ph1 : ph0;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_slab) + ((int64_t)ph * a.hkv + g) * C::PAGE;
+    const int v_lane = (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 3) & 1)) * 16);
+    const uint32_t off = (inst % (D / 32)) * 1024 + v_lane;
+    dma16_s(vbase, off, vb + inst * 1024);
+}
+template <int D>
+__device__ __forceinline__ void issue_v(const ExtendArgs& a, uint32_t vb, int32_t ph0, int32_t ph1, int32_t g,
+                                        int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < XCfg<D>::DMA; ++i) issue_v_part<D>(a, vb, ph0, ph1, g, wave, lane, i);
+}
+
+// Online softmax of one score tile s (lane: query row col, kv tokens
+// 8h..8h+7 and 16+8h..16+8h+7 of the tile at t0), masked where needed; returns
+// the two B operands of the value product (P^T, bf16) and updates the
+// running max / sum.  `rescale` is called with the factor for O when the
+// running max is raised.
+template <typename Rescale>
+__device__ __forceinline__ void softmax_tile(f32x16& s, int32_t t0, bool whole, int32_t row_lo, int32_t row_hi,
+                                             int h, float score_scale, float& m_run, float& l_run, u32x4 (&pb)[2],
+                                             Rescale rescale) {
+    if (!whole) {
+        // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
+        const int32_t lo_l = row_lo - t0 - 8 * h, hi_l = row_hi - t0 - 8 * h;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int c = e + ((e >> 3) << 3);
+            s[e] = ((c >= lo_l) & (c <= hi_l)) ? s[e] : -INFINITY;
+        }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    mx = max_halves(mx) * score_scale;
+    const bool raise = mx > m_run + kRescale;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float al = raise ? alpha : 1.f;
+        l_run *= al;
+        m_run = m_new;
+        rescale(al);
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], score_scale, -m_use));
+        l_run += s[e];
     }
 #pragma unroll
-    for (int i = 0; i < C::DMA / 2; ++i) {
-        const int inst = wave + C::NW * i;
-        const int p = inst / (D / 32);
-        const uint32_t off = (inst % (D / 32)) * 1024 + v_lane;
-        dma16_s(vbase[p], off, vb + inst * 1024);
+    for (int st = 0; st < 2; ++st)
+        pb[st] = u32x4{cvt_pk_bf16(s[8 * st + 0], s[8 * st + 1]), cvt_pk_bf16(s[8 * st + 2], s[8 * st + 3]),
+                       cvt_pk_bf16(s[8 * st + 4], s[8 * st + 5]), cvt_pk_bf16(s[8 * st + 6], s[8 * st + 7])};
+}
+
+// One wavefront's step of the software pipeline: the score product of tile
+// t+1 (kb) and the value product of tile t (vb, operands pb) interleaved, so
+// the independent MFMA chains keep the matrix core busy.  Each K or V operand
+// read from LDS feeds the MFMAs of all NRB row blocks of the wavefront.  The
+// LDS operands are prefetched PF steps ahead in rotating registers, and a
+// scheduling barrier closes every step so the compiler keeps this order (and
+// this register footprint) instead of hoisting every load.  copy(j) issues
+// copy j of the next tiles' global -> LDS copies, one per step from the first
+// on, so the copies' address traffic overlaps the matrix work instead of
+// stalling every wavefront at the top of the step.  With HAVE_S = false only
+// the value product runs (the last tile).
+template <int D, bool HAVE_S, typename Copy>
+__device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[4], int v_off,
+                                          const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
+                                          const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
+                                          f32x16 (&o)[16], int n_copies, Copy copy) {
+    constexpr int KK = D / 16, MT = D / 32, PF = 4, NRB = XCfg<D>::NRB;
+    auto ld_k = [&](int i) { return *reinterpret_cast<const u32x4*>(kb + k_off[i & 3] + (i >> 2) * 128); };
+    // value step i: kv half st = i / MT, output tile m = i % MT
+    auto ld_v = [&](int i) {
+        return *reinterpret_cast<const u32x4*>(vb + (i / MT) * (16 * D * 2) + (i % MT) * 1024 + v_off);
+    };
+    u32x4 kr[PF], vr[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        vr[p] = ld_v(p);
+        if constexpr (HAVE_S) kr[p] = ld_k(p);
+    }
+#pragma unroll
+    for (int i = 0; i < KK; ++i) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            if (i == 0) asm_mfma_agpr_nop(o[rb * MT], vr[0], pb[rb][0]);
+            else asm_mfma_agpr(o[rb * MT + i % MT], vr[i % PF], pb[rb][i / MT]);
+            if constexpr (HAVE_S) {
+                if (i == 0) s[rb] = asm_mfma_first(kr[0], qreg[rb][0]);
+                else asm_mfma_acc(s[rb], kr[i % PF], qreg[rb][i]);
+            }
+        }
+        if (i + PF < KK) {
+            vr[i % PF] = ld_v(i + PF);
+            if constexpr (HAVE_S) kr[i % PF] = ld_k(i + PF);
+        }
+        if (i < n_copies) copy(i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (HAVE_S) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) asm_mfma_drain(s[rb]);
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) {
     using C = XCfg<D>;
+    constexpr int NRB = C::NRB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
-    // grid (Hkv, B, row blocks): dispatch walks x fastest, so every (head,
-    // sequence) pair gets its heaviest (last) row block before any lighter one
-    const int32_t g = blockIdx.x, b = blockIdx.y;
-    const int32_t blk = gridDim.z - 1 - blockIdx.z;
+    // grid (Hkv, row blocks, B): dispatch walks x fastest, then y, then z, so
+    // the workgroups start heaviest first (longest-processing-time order): the
+    // sequence of rank z in decreasing kv end (prefix + chunk; ties by index)
+    // with its row blocks from the last (longest kv range) down.  Up to
+    // kRankedSeqs sequences are ranked; beyond that they run in index order.
+    const int32_t g = blockIdx.x;
+    const int32_t blk = gridDim.y - 1 - blockIdx.y;
+    int32_t b = blockIdx.z;
+    const int32_t B = gridDim.z;
+    if (B > 1 && B <= kRankedSeqs) {
+        __shared__ int32_t s_key[kRankedSeqs];
+        __shared__ int32_t s_seq;
+        if (tid < B) s_key[tid] = min(a.cu_q[tid + 1] - a.cu_q[tid], a.max_q_len) + a.prefix_lens[tid];
+        __syncthreads();
+        if (tid < B) {
+            const int32_t key = s_key[tid];
+            int32_t rank = 0;
+            for (int32_t j = 0; j < B; ++j) {
+                const int32_t kj = s_key[j];
+                rank += (kj > key) || (kj == key && j < tid);
+            }
+            if (rank == (int32_t)blockIdx.z) s_seq = tid;
+        }
+        __syncthreads();
+        b = s_seq;
+    }
     const int32_t G = a.group;
     const int32_t q0 = a.cu_q[b];
     const int32_t n = min(a.cu_q[b + 1] - q0, a.max_q_len);
@@ -219,18 +377,26 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     const int32_t hi = min(prefix + tok_last + 1, a.max_kv_len);          // kv range of the workgroup
     const int32_t lo = (a.window > 0) ? max(0, prefix + tok_first - a.window + 1) : 0;
 
-    // this lane's query row (score column) and its visible kv range [row_lo, row_hi]
-    const int32_t wrow0 = row0 + wave * 32;
+    // this lane's query rows (one per row block: score column) and their
+    // visible kv ranges [row_lo, row_hi]; a row block past the chunk is idle
+    const int32_t wrow0 = row0 + wave * 32 * NRB;
     const bool wave_live = wrow0 < rows;
-    const int32_t my_row = wrow0 + col;
-    const bool row_ok = my_row < rows;
-    const int32_t my_tok = row_ok ? my_row / G : 0, my_head = my_row % G;
-    const int32_t my_pos = prefix + my_tok;
-    const int32_t row_hi = min(my_pos, hi - 1);
-    const int32_t row_lo = (a.window > 0) ? my_pos - a.window + 1 : -(1 << 30);
-    // the wavefront's extreme positions, for the "tile visible to all rows" test
-    const int32_t w_pmin = prefix + min(n - 1, wrow0 / G);
-    const int32_t w_pmax = prefix + min(n - 1, (wrow0 + 31) / G);
+    int32_t my_tok[NRB], my_head[NRB], row_lo[NRB], row_hi[NRB], w_pmin[NRB], w_pmax[NRB];
+    bool row_ok[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int32_t r0 = wrow0 + 32 * rb;
+        const int32_t my_row = r0 + col;
+        row_ok[rb] = my_row < rows;
+        my_tok[rb] = row_ok[rb] ? my_row / G : 0;
+        my_head[rb] = my_row % G;
+        const int32_t my_pos = prefix + my_tok[rb];
+        row_hi[rb] = min(my_pos, hi - 1);
+        row_lo[rb] = (a.window > 0) ? my_pos - a.window + 1 : -(1 << 30);
+        // the row block's extreme positions, for the "tile visible to all rows" test
+        w_pmin[rb] = prefix + min(n - 1, r0 / G);
+        w_pmax[rb] = prefix + min(n - 1, (r0 + 31) / G);
+    }
 
     const int32_t t_begin = (lo / kTile) * kTile;
     const int32_t n_tiles = (hi - t_begin + kTile - 1) / kTile;
@@ -244,31 +410,45 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         if (pg < a.max_pages) ph = pt[pg];
         return ((uint32_t)ph < (uint32_t)a.num_pages) ? ph : 0;
     };
+    // ids holds pages [64 c_ids, +64), ids_next the next 64.  The V copy lags
+    // the K copy by one tile (two pages), so both read inside this window.
+    int32_t c_ids = 0;
     int32_t ids = load_ids(0);
-    int32_t ids_next = (n_tiles > 32) ? load_ids(1) : 0;
+    int32_t ids_next = (2 * n_tiles > 64) ? load_ids(1) : 0;
+    auto page_id = [&](int32_t rp) -> int32_t {
+        const int32_t r = rp - 64 * c_ids;
+        return (r < 64) ? __builtin_amdgcn_readlane(ids, r) : __builtin_amdgcn_readlane(ids_next, r - 64);
+    };
 
-    // Q^T operand: lane holds Q[row col][16 kk + 8 h .. +8]; rows past the
-    // chunk read token 0 of the chunk and are never written back
-    u32x4 qreg[C::KK];
-    {
-        const uint16_t* qp = a.q + ((int64_t)(q0 + my_tok) * a.hq + (int64_t)g * G + my_head) * D + 8 * h;
+    // Q^T operands: lane holds Q[row col of block rb][16 kk + 8 h .. +8]; rows
+    // past the chunk read token 0 of the chunk and are never written back
+    u32x4 qreg[NRB][C::KK];
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) qreg[kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
+    for (int rb = 0; rb < NRB; ++rb) {
+        const uint16_t* qp = a.q + ((int64_t)(q0 + my_tok[rb]) * a.hq + (int64_t)g * G + my_head[rb]) * D + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) qreg[rb][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
     }
     wait_vm<0>();
 
     const uint32_t lds0 = lds_addr_of(lds);
-    if (n_tiles > 0)
-        issue_tile<D>(a, lds0, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), g, wave, lane);
-
-    f32x16 o[C::MT];
-#pragma unroll
-    for (int m = 0; m < C::MT; ++m) o[m] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-    if constexpr (D == 512) {
-#pragma unroll
-        for (int m = 0; m < C::MT; ++m) pin_agpr(o[m]);
-    }
+    auto kslot = [&](int32_t t) -> uint32_t { return lds0 + (t & 1) * C::HALF; };
+    auto vslot = [&](int32_t t) -> uint32_t { return lds0 + 2 * C::HALF + (t & 1) * C::HALF; };
+    auto copy_k = [&](int32_t t) {
+        issue_k<D>(a, kslot(t), page_id(2 * t), page_id(2 * t + 1), g, wave, lane);
+    };
+    // the V copy (the lagging one) leaves batch c_ids at page rp: slide the window
+    auto slide_ids = [&](int32_t rp) {
+        if (rp >= 64 * (c_ids + 1)) {
+            ids = ids_next;
+            ++c_ids;
+            if (64 * (c_ids + 1) < 2 * n_tiles) ids_next = load_ids(c_ids + 1);
+        }
+    };
+    auto copy_v = [&](int32_t t) {
+        slide_ids(2 * t);
+        issue_v<D>(a, vslot(t), page_id(2 * t), page_id(2 * t + 1), g, wave, lane);
+    };
 
     // LDS offsets this lane reads: K row tau(col), granules (2 kk + h) ^ key
     int k_off[4];
@@ -276,132 +456,146 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         const int j = col >> 3, hh = (col >> 2) & 1, i = col & 3;
         const int tk = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) k_off[s] = tk * C::KROW + (((2 * s + h) ^ k_swz(tk)) * 16);
+        for (int s4 = 0; s4 < 4; ++s4) k_off[s4] = tk * C::KROW + (((2 * s4 + h) ^ k_swz(tk)) * 16);
     }
     const int v_off = col * 32 + ((h ^ ((col >> 2) & 1)) * 16);
 
-    for (int32_t it = 0; it < n_tiles; ++it) {
+    // O^T tiles: row block rb, output tile m at o[rb * MT + m] (16 tiles)
+    f32x16 o[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) o[m] = f32x16{};
+    float m_run[NRB], l_run[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) pin_agpr(o[m]);
+    // the zeros were written by the VALU; the value MFMAs (inline asm, so the
+    // compiler does not separate them) read the tiles as SrcC
+    asm volatile("s_nop 4" ::: "memory");
+    auto is_whole = [&](int32_t t0, int rb) -> bool {
+        return (t0 + kTile - 1 <= min(w_pmin[rb], hi - 1)) && (a.window == 0 || w_pmax[rb] - a.window + 1 <= t0);
+    };
+    // softmax of tile t0 for every row block; a rescale of row block rb's O
+    // first lets every value MFMA that wrote it land (settle_tiles)
+    f32x16 s[NRB];
+    u32x4 pb[NRB][2];
+    auto softmax_all = [&](int32_t t0) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            softmax_tile(s[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], h, a.score_scale, m_run[rb],
+                         l_run[rb], pb[rb], [&](float al) {
+                             settle_tiles(o);
+#pragma unroll
+                             for (int m = 0; m < C::MT; ++m) agpr_scale(o[rb * C::MT + m], al);
+                         });
+        }
+    };
+    // zeroes V of tokens outside [lo, hi) in V tile t: never-written slots may hold NaN
+    auto zero_v_edges = [&](int32_t t) {
+        const int32_t t0 = t_begin + t * kTile;
+        if (t0 >= lo && t0 + kTile <= hi) return;
+        uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
+        for (int idx = tid; idx < 4 * D; idx += C::THREADS) {
+            const int p = idx / (2 * D), d = (idx >> 1) % D, hp = idx & 1;
+            const int half = hp ^ ((d >> 2) & 1);
+            const int32_t tb = t0 + 16 * p + 8 * half;
+            u32x4* gp = reinterpret_cast<u32x4*>(vbuf + p * C::PAGE + d * 32 + hp * 16);
+            u32x4 v = *gp;
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int32_t tt = tb + 2 * e;
+                const uint32_t keep = ((tt >= lo && tt < hi) ? 0xffffu : 0u) |
+                                      ((tt + 1 >= lo && tt + 1 < hi) ? 0xffff0000u : 0u);
+                w[e] &= keep;
+            }
+            *gp = u32x4{w[0], w[1], w[2], w[3]};
+        }
+        lds_barrier();
+    };
+
+    // ---- prologue: K(0), V(0), K(1); scores and softmax of tile 0 ----------------
+    if (n_tiles > 0) {
+        copy_k(0);
+        copy_v(0);
+        if (n_tiles > 1) copy_k(1);
         wait_vm<0>();
         lds_barrier();
-        const int32_t t0 = t_begin + it * kTile;
-        if (it + 1 < n_tiles) {
-            const int32_t rp = 2 * (it + 1);            // page of the next tile, relative to page0
-            if ((rp & 63) == 0) {
-                ids = ids_next;
-                if (it + 33 < n_tiles) ids_next = load_ids((rp >> 6) + 1);
-            }
-            issue_tile<D>(a, lds0 + ((it + 1) % C::NBUF) * C::TILE, __builtin_amdgcn_readlane(ids, rp & 63),
-                          __builtin_amdgcn_readlane(ids, (rp & 63) + 1), g, wave, lane);
-        }
-        uint8_t* kbuf = lds + (it % C::NBUF) * C::TILE;
-        uint8_t* vbuf = kbuf + 2 * C::PAGE;
-        if (t0 < lo || t0 + kTile > hi) {
-            // zero V of tokens outside [lo, hi): never-written slots may hold NaN
-            for (int idx = tid; idx < 4 * D; idx += C::THREADS) {
-                const int p = idx / (2 * D), d = (idx >> 1) % D, hp = idx & 1;
-                const int half = hp ^ ((d >> 2) & 1);
-                const int32_t tb = t0 + 16 * p + 8 * half;
-                u32x4* gp = reinterpret_cast<u32x4*>(vbuf + p * C::PAGE + d * 32 + hp * 16);
-                u32x4 v = *gp;
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int32_t t = tb + 2 * e;
-                    const uint32_t keep = ((t >= lo && t < hi) ? 0xffffu : 0u) |
-                                          ((t + 1 >= lo && t + 1 < hi) ? 0xffff0000u : 0u);
-                    w[e] &= keep;
-                }
-                *gp = u32x4{w[0], w[1], w[2], w[3]};
-            }
-            lds_barrier();
-        }
         if (wave_live) {
-        // ---- scores S^T[kv][row col] -------------------------------------------------
-        f32x16 s;
-        if constexpr (D == 512) {
-            s = asm_mfma_first(*reinterpret_cast<const u32x4*>(kbuf + k_off[0]), qreg[0]);
+            const uint8_t* kbuf = lds + 0;
 #pragma unroll
-            for (int kk = 1; kk < C::KK; ++kk)
-                asm_mfma_acc(s, *reinterpret_cast<const u32x4*>(kbuf + k_off[kk & 3] + (kk >> 2) * 128), qreg[kk]);
-            asm_mfma_drain(s);
-        } else {
-            s = f32x16{};
+            for (int rb = 0; rb < NRB; ++rb) {
+                s[rb] = asm_mfma_first(*reinterpret_cast<const u32x4*>(kbuf + k_off[0]), qreg[rb][0]);
 #pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) {
-                const u32x4 ka = *reinterpret_cast<const u32x4*>(kbuf + k_off[kk & 3] + (kk >> 2) * 128);
-                s = mfma_32x32x16(ka, qreg[kk], s);
+                for (int kk = 1; kk < C::KK; ++kk)
+                    asm_mfma_acc(s[rb], *reinterpret_cast<const u32x4*>(kbuf + k_off[kk & 3] + (kk >> 2) * 128),
+                                 qreg[rb][kk]);
+                asm_mfma_drain(s[rb]);
             }
-        }
-        const bool whole = (t0 + kTile - 1 <= min(w_pmin, hi - 1)) &&
-                           (a.window == 0 || w_pmax - a.window + 1 <= t0);
-        if (!whole) {
-            // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
-            const int32_t lo_l = row_lo - t0 - 8 * h, hi_l = row_hi - t0 - 8 * h;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int c = e + ((e >> 3) << 3);
-                s[e] = ((c >= lo_l) & (c <= hi_l)) ? s[e] : -INFINITY;
-            }
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = max_halves(mx) * a.score_scale;
-        const bool raise = mx > m_run + kRescale;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-            const float m_new = raise ? mx : m_run;
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            const float al = raise ? alpha : 1.f;
-            l_run *= al;
-            m_run = m_new;
-            if constexpr (D == 512) {
-#pragma unroll
-                for (int m = 0; m < C::MT; ++m) agpr_scale(o[m], al);
-            } else {
-#pragma unroll
-                for (int m = 0; m < C::MT; ++m) o[m] *= al;
-            }
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.score_scale, -m_use));
-            l_run += s[e];
-        }
-        u32x4 pb[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-            pb[st] = u32x4{cvt_pk_bf16(s[8 * st + 0], s[8 * st + 1]), cvt_pk_bf16(s[8 * st + 2], s[8 * st + 3]),
-                           cvt_pk_bf16(s[8 * st + 4], s[8 * st + 5]), cvt_pk_bf16(s[8 * st + 6], s[8 * st + 7])};
-
-        // ---- values O^T[d][row] += V^T[d][kv] P^T[kv][row] ---------------------------
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int m = 0; m < C::MT; ++m) {
-                const u32x4 va = *reinterpret_cast<const u32x4*>(vbuf + st * C::PAGE + m * 1024 + v_off);
-                o[m] = mfma_32x32x16(va, pb[st], o[m]);
-            }
-        }
-        }
-        if constexpr (D == 512) {
-#pragma unroll
-            for (int m = 0; m < C::MT; ++m) pin_agpr(o[m]);
+            softmax_all(t_begin);
         }
     }
 
+    // ---- steady state: step t = scores of tile t+1 with values of tile t --------
+    // (the last step, values only, is peeled off so that the loop body has one
+    // path and the accumulator tiles stay put in the AGPR file)
+    for (int32_t t = 0; t + 1 < n_tiles; ++t) {
+        wait_vm<0>();              // V(t) and K(t+1), copied during the previous step
+        lds_barrier();             // ... for every wave; and K(t), V(t-1) are no longer read
+        // copies of this step: V(t+1) into V(t-1)'s slot, K(t+2) into K(t)'s
+        slide_ids(2 * (t + 1));
+        const int32_t pv0 = page_id(2 * t + 2), pv1 = page_id(2 * t + 3);
+        const bool k_next = t + 2 < n_tiles;
+        const int32_t pk0 = k_next ? page_id(2 * t + 4) : 0, pk1 = k_next ? page_id(2 * t + 5) : 0;
+        const uint32_t vs = vslot(t + 1), ks = kslot(t + 2);
+        auto copy = [&](int j) {
+            if (j < C::DMA) issue_v_part<D>(a, vs, pv0, pv1, g, wave, lane, j);
+            else issue_k_part<D>(a, ks, pk0, pk1, g, wave, lane, j - C::DMA);
+        };
+        const int n_copies = k_next ? 2 * C::DMA : C::DMA;
+        zero_v_edges(t);
+        if (wave_live) {
+            const uint8_t* kbuf = lds + ((t + 1) & 1) * C::HALF;
+            const uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
+            step_mfma<D, true>(kbuf, vbuf, k_off, v_off, qreg, pb, s, o, n_copies, copy);
+            softmax_all(t_begin + (t + 1) * kTile);
+        } else {
+            for (int j = 0; j < n_copies; ++j) copy(j);     // a wavefront with no rows still copies its share
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) pin_agpr(o[m]);
+    }
+    if (n_tiles > 0) {
+        const int32_t t = n_tiles - 1;
+        wait_vm<0>();
+        lds_barrier();
+        zero_v_edges(t);
+        if (wave_live) {
+            const uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
+            step_mfma<D, false>(lds, vbuf, k_off, v_off, qreg, pb, s, o, 0, [](int) {});
+        }
+        settle_tiles(o);   // the last value MFMAs have landed before the output reads them
+    }
+
     wait_vm<0>();   // no copy may still be landing in LDS when the workgroup ends
-    l_run = sum_halves(l_run);
-    if (!row_ok) return;
-    const float inv = 1.0f / l_run;
-    uint16_t* op = a.out + ((int64_t)(q0 + my_tok) * a.hq + (int64_t)g * G + my_head) * D;
 #pragma unroll
-    for (int m = 0; m < C::MT; ++m) {
+    for (int rb = 0; rb < NRB; ++rb) {
+        const float l_tot = sum_halves(l_run[rb]);
+        if (!row_ok[rb]) continue;
+        const float inv = 1.0f / l_tot;
+        uint16_t* op = a.out + ((int64_t)(q0 + my_tok[rb]) * a.hq + (int64_t)g * G + my_head[rb]) * D;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = 32 * m + 8 * j + 4 * h;
-            *reinterpret_cast<u32x2*>(op + d) = u32x2{cvt_pk_bf16(o[m][4 * j] * inv, o[m][4 * j + 1] * inv),
-                                                      cvt_pk_bf16(o[m][4 * j + 2] * inv, o[m][4 * j + 3] * inv)};
+        for (int m = 0; m < C::MT; ++m) {
+            const f32x16& om = o[rb * C::MT + m];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 32 * m + 8 * j + 4 * h;
+                *reinterpret_cast<u32x2*>(op + d) = u32x2{cvt_pk_bf16(om[4 * j] * inv, om[4 * j + 1] * inv),
+                                                          cvt_pk_bf16(om[4 * j + 2] * inv, om[4 * j + 3] * inv)};
+            }
         }
     }
 }
@@ -432,11 +626,11 @@ int launch_extend(const ExtendLaunch& s, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s.head_dim == 256) {
         using C = XCfg<256>;
-        const dim3 grid(s.hkv, s.num_seqs, (unsigned)((rows + C::ROWS - 1) / C::ROWS));
+        const dim3 grid(s.hkv, (unsigned)((rows + C::ROWS - 1) / C::ROWS), s.num_seqs);
         launch(PAKV_TIME_EXTEND, extend_kernel<256>, grid, dim3(C::THREADS), 0, st, a);
     } else {
         using C = XCfg<512>;
-        const dim3 grid(s.hkv, s.num_seqs, (unsigned)((rows + C::ROWS - 1) / C::ROWS));
+        const dim3 grid(s.hkv, (unsigned)((rows + C::ROWS - 1) / C::ROWS), s.num_seqs);
         launch(PAKV_TIME_EXTEND, extend_kernel<512>, grid, dim3(C::THREADS), 0, st, a);
     }
     return (int)hipGetLastError();

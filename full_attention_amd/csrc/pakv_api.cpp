@@ -344,6 +344,11 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
         return fail(PAKV_ERR_UNSUPPORTED, "extend on an int8 layer is not built");
     const auto& S = map->layers[L.source];
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
+    // grid (Hkv, row blocks of 128 (token, head) rows, sequences)
+    const int64_t row_blocks = ((int64_t)max_q_len * (L.desc.num_q_heads / L.desc.num_kv_heads) + 127) / 128;
+    if (row_blocks > 65535 || num_seqs > 65535)
+        return fail(PAKV_ERR_UNSUPPORTED, "extend grid too large: %lld row blocks, %d sequences (65535 each at most)",
+                    (long long)row_blocks, num_seqs);
     ExtendLaunch a;
     a.slab = view_of(S);
     a.page_table = pages->page_table;
