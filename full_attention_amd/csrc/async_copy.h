@@ -24,6 +24,16 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
         : "memory");
 }
 
+// A wave-uniform pointer as the scalar operand of a copy: when the compiler
+// cannot prove the value uniform it would otherwise hand the asm a VGPR pair.
+// (Both halves go through uint32_t so the high half is not sign-extended.)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>((uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo));
+}
+
 // Same copy from a wave-uniform base address plus a per-lane 32-bit byte
 // offset (the scalar-base form keeps one VGPR per copy instead of two).
 __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds_addr) {
@@ -35,7 +45,43 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
         "global_load_lds_dwordx4 %2, %3\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(base)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
+        : "memory");
+}
+
+// Runs of copies from one wave-uniform base with M0 written once: copy i
+// reads base + voff_i + 1024 i into LDS [lds_addr + 1024 i, +1024) (the
+// instruction's immediate offset is added to both the global and the LDS
+// address).  A wavefront runs one instruction at a time, so a copy costs as
+// many issue slots as the scalar work around it; this keeps it to two per
+// copy.
+__device__ __forceinline__ void dma16_s_x4(const void* base, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                           uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "global_load_lds_dwordx4 %3, %6 offset:1024\n\t"
+        "global_load_lds_dwordx4 %4, %6 offset:2048\n\t"
+        "global_load_lds_dwordx4 %5, %6 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(uniform_ptr(base))
+        : "memory");
+}
+__device__ __forceinline__ void dma16_s_x2(const void* base, uint32_t v0, uint32_t v1, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %4\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(v0), "v"(v1), "s"(uniform_ptr(base))
         : "memory");
 }
 

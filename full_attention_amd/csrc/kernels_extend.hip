@@ -51,6 +51,11 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 constexpr int kTile = 32;            // kv tokens per staged tile (two pages)
 constexpr int kRankedSeqs = 256;     // sequences ordered by weight at dispatch (one per thread)
 constexpr float kRescale = 8.0f;     // raise the running max only past 2^8
+constexpr int kRuns = 4;             // copy runs per step: V(t+1) and K(t+2), one per page
+#ifndef PAKV_RUN_GAP
+#define PAKV_RUN_GAP 1
+#endif
+constexpr int kRunGapSet = PAKV_RUN_GAP;   // loop steps between copy runs (0: spread evenly)
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -182,56 +187,56 @@ struct XCfg {
     static constexpr int KROW = D * 2;                  // bytes per K row
     static constexpr int PAGE = 16 * D * 2;             // bytes per (page, head) block
     static constexpr int HALF = 2 * PAGE;               // K (or V) of one 32-token tile
-    static constexpr int DMA = HALF / 1024 / NW;        // 1 KiB copies per wave per K (or V) tile
+    static constexpr int PP = PAGE / 1024;              // 1 KiB pieces per (page, head) block
+    static constexpr int NI = PP / NW;                  // pieces per wavefront per page
     static constexpr int LDS = 4 * HALF;                // K ring of 2 tiles, V ring of 2 tiles
     static constexpr int KK = D / 16;                   // 16-dim steps of the score product
     static constexpr int MT = D / 32;                   // 32-dim tiles of the output
     static_assert(KK == 2 * MT, "one score MFMA per value MFMA");
-    static_assert(DMA * NW * 1024 == HALF, "tile copies must split evenly");
+    static_assert(NI * NW == PP && (NI == 2 || NI == 4), "page copies must split into runs of 2 or 4");
 };
 
-// Copies the K rows of the tile whose two pages are physical pages ph0, ph1.
-// Copy `inst` fills LDS bytes [1024 inst, +1024): K rows
-// tk = inst * 64 / (D / 8) + lane / (D / 8), with granule colp ^ key(tk) of
-// row tk landing at granule colp.
+// Each (page, head) block of K or V is PP = PAGE / 1 KiB pieces; wavefront w
+// copies pieces NI w .. NI w + NI - 1 (NI = PP / NW) of every page of a tile,
+// piece q of page p landing at LDS bytes [1024 (PP p + q), +1024), as one run
+// of NI copies with M0 written once (copy i of a run carries the immediate
+// offset 1024 i, added to both addresses).
+//
+// K piece q holds the page's rows tk = (64 q + lane) / GR (GR 16-byte
+// granules per row), granule colp ^ key(tk) of row tk landing at granule colp;
+// V piece q holds dims d = 32 q + lane / 2 of the page, half (lane & 1) ^
+// bit 2 of d.  The per-lane source offsets (less 1024 i) are the same for
+// every page and every tile, so they are formed once.
 template <int D>
-__device__ __forceinline__ void issue_k_part(const ExtendArgs& a, uint32_t kb, int32_t ph0, int32_t ph1, int32_t g,
-                                             int wave, int lane, int i) {
+__device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t (&k_voff)[XCfg<D>::NI], uint32_t& v_voff) {
     using C = XCfg<D>;
-    constexpr int GR = C::KROW / 16;                    // granules per K row (32 or 64)
-    const int inst = wave + C::NW * i;                  // wave-uniform
-    const int32_t ph = ((inst * 64) / (16 * GR)) ? ph1 : ph0;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_slab) + ((int64_t)ph * a.hkv + g) * C::PAGE;
+    constexpr int GR = C::KROW / 16;
     const int colp = lane % GR;
-    const int tk = (inst * 64 + lane) / GR;
-    const uint32_t off = (tk & 15) * C::KROW + ((colp ^ k_swz(tk)) * 16);
-    dma16_s(kbase, off, kb + inst * 1024);
-}
-template <int D>
-__device__ __forceinline__ void issue_k(const ExtendArgs& a, uint32_t kb, int32_t ph0, int32_t ph1, int32_t g,
-                                        int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < XCfg<D>::DMA; ++i) issue_k_part<D>(a, kb, ph0, ph1, g, wave, lane, i);
+    for (int i = 0; i < C::NI; ++i) {
+        const int q = C::NI * wave + i;
+        const int tk = (q * 64 + lane) / GR;
+        k_voff[i] = (uint32_t)(tk * C::KROW + ((colp ^ k_swz(tk)) * 16) - 1024 * i);
+    }
+    v_voff = (uint32_t)(C::NI * wave * 1024 + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 3) & 1)) * 16));
 }
 
-// Copies the V pages of the same tile: copy `inst` fills dims
-// d = 32 inst + lane / 2 (page inst / (D / 32)), half (lane & 1) ^ bit 2 of d.
+// One wavefront's run of page p of a tile (LDS slot base `slot`) from the
+// block at `src` (K: per-piece offsets k_voff; V: v_voff for every piece).
 template <int D>
-__device__ __forceinline__ void issue_v_part(const ExtendArgs& a, uint32_t vb, int32_t ph0, int32_t ph1, int32_t g,
-                                             int wave, int lane, int i) {
+__device__ __forceinline__ void copy_k_run(const uint8_t* src, const uint32_t (&k_voff)[XCfg<D>::NI], uint32_t slot,
+                                           int p, int wave) {
     using C = XCfg<D>;
-    const int inst = wave + C::NW * i;
-    const int32_t ph = (inst / (D / 32)) ? ph1 : ph0;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_slab) + ((int64_t)ph * a.hkv + g) * C::PAGE;
-    const int v_lane = (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 3) & 1)) * 16);
-    const uint32_t off = (inst % (D / 32)) * 1024 + v_lane;
-    dma16_s(vbase, off, vb + inst * 1024);
+    const uint32_t dst = slot + (C::PP * p + C::NI * wave) * 1024;
+    if constexpr (C::NI == 4) dma16_s_x4(src, k_voff[0], k_voff[1], k_voff[2], k_voff[3], dst);
+    else dma16_s_x2(src, k_voff[0], k_voff[1], dst);
 }
 template <int D>
-__device__ __forceinline__ void issue_v(const ExtendArgs& a, uint32_t vb, int32_t ph0, int32_t ph1, int32_t g,
-                                        int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < XCfg<D>::DMA; ++i) issue_v_part<D>(a, vb, ph0, ph1, g, wave, lane, i);
+__device__ __forceinline__ void copy_v_run(const uint8_t* src, uint32_t v_voff, uint32_t slot, int p, int wave) {
+    using C = XCfg<D>;
+    const uint32_t dst = slot + (C::PP * p + C::NI * wave) * 1024;
+    if constexpr (C::NI == 4) dma16_s_x4(src, v_voff, v_voff, v_voff, v_voff, dst);
+    else dma16_s_x2(src, v_voff, v_voff, dst);
 }
 
 // Online softmax of one score tile s (lane: query row col, kv tokens
@@ -284,16 +289,18 @@ __device__ __forceinline__ void softmax_tile(f32x16& s, int32_t t0, bool whole, 
 // LDS operands are prefetched PF steps ahead in rotating registers, and a
 // scheduling barrier closes every step so the compiler keeps this order (and
 // this register footprint) instead of hoisting every load.  copy(j) issues
-// copy j of the next tiles' global -> LDS copies, one per step from the first
-// on, so the copies' address traffic overlaps the matrix work instead of
-// stalling every wavefront at the top of the step.  With HAVE_S = false only
-// the value product runs (the last tile).
+// run j (of at most kRuns) of the next tiles' global -> LDS copies, one run
+// every kRunGap steps of the loop, so the copies overlap the matrix work
+// instead of stalling every wavefront at the top of the step.  With
+// HAVE_S = false only the value product runs (the last tile).
 template <int D, bool HAVE_S, typename Copy>
 __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[4], int v_off,
                                           const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
                                           const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
                                           f32x16 (&o)[16], int n_copies, Copy copy) {
     constexpr int KK = D / 16, MT = D / 32, PF = 4, NRB = XCfg<D>::NRB;
+    constexpr int kRunGap = kRunGapSet > 0 ? kRunGapSet : KK / kRuns;
+    static_assert((kRuns - 1) * kRunGap < KK, "every copy run needs a loop step");
     auto ld_k = [&](int i) { return *reinterpret_cast<const u32x4*>(kb + k_off[i & 3] + (i >> 2) * 128); };
     // value step i: kv half st = i / MT, output tile m = i % MT
     auto ld_v = [&](int i) {
@@ -320,7 +327,9 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
             vr[i % PF] = ld_v(i + PF);
             if constexpr (HAVE_S) kr[i % PF] = ld_k(i + PF);
         }
-        if (i < n_copies) copy(i);
+        if (i % kRunGap == 0 && i / kRunGap < kRuns) {
+            if (i / kRunGap < n_copies) copy(i / kRunGap);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (HAVE_S) {
@@ -410,15 +419,23 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         if (pg < a.max_pages) ph = pt[pg];
         return ((uint32_t)ph < (uint32_t)a.num_pages) ? ph : 0;
     };
-    // ids holds pages [64 c_ids, +64), ids_next the next 64.  The V copy lags
-    // the K copy by one tile (two pages), so both read inside this window.
+    // ids holds pages [64 c_ids, +64), ids_next the next 64.  Only the K copy
+    // reads page ids (V(t) copies the pages K(t) did, a step later), and a
+    // tile's two pages never straddle a batch.
     int32_t c_ids = 0;
     int32_t ids = load_ids(0);
     int32_t ids_next = (2 * n_tiles > 64) ? load_ids(1) : 0;
-    auto page_id = [&](int32_t rp) -> int32_t {
-        const int32_t r = rp - 64 * c_ids;
-        return (r < 64) ? __builtin_amdgcn_readlane(ids, r) : __builtin_amdgcn_readlane(ids_next, r - 64);
+    auto page_id = [&](int32_t rp) -> int32_t { return __builtin_amdgcn_readlane(ids, rp - 64 * c_ids); };
+    // moves the window so that it holds page rp (rp grows by two per step)
+    auto slide_ids = [&](int32_t rp) {
+        if (rp >= 64 * (c_ids + 1)) {
+            ids = ids_next;
+            ++c_ids;
+            if (64 * (c_ids + 1) < 2 * n_tiles) ids_next = load_ids(c_ids + 1);
+        }
     };
+    // byte offset of a physical page's block of KV head g in either slab
+    auto page_off = [&](int32_t ph) -> int64_t { return ((int64_t)ph * a.hkv + g) * C::PAGE; };
 
     // Q^T operands: lane holds Q[row col of block rb][16 kk + 8 h .. +8]; rows
     // past the chunk read token 0 of the chunk and are never written back
@@ -434,21 +451,10 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     const uint32_t lds0 = lds_addr_of(lds);
     auto kslot = [&](int32_t t) -> uint32_t { return lds0 + (t & 1) * C::HALF; };
     auto vslot = [&](int32_t t) -> uint32_t { return lds0 + 2 * C::HALF + (t & 1) * C::HALF; };
-    auto copy_k = [&](int32_t t) {
-        issue_k<D>(a, kslot(t), page_id(2 * t), page_id(2 * t + 1), g, wave, lane);
-    };
-    // the V copy (the lagging one) leaves batch c_ids at page rp: slide the window
-    auto slide_ids = [&](int32_t rp) {
-        if (rp >= 64 * (c_ids + 1)) {
-            ids = ids_next;
-            ++c_ids;
-            if (64 * (c_ids + 1) < 2 * n_tiles) ids_next = load_ids(c_ids + 1);
-        }
-    };
-    auto copy_v = [&](int32_t t) {
-        slide_ids(2 * t);
-        issue_v<D>(a, vslot(t), page_id(2 * t), page_id(2 * t + 1), g, wave, lane);
-    };
+    const uint8_t* k_src = reinterpret_cast<const uint8_t*>(a.k_slab);
+    const uint8_t* v_src = reinterpret_cast<const uint8_t*>(a.v_slab);
+    uint32_t k_voff[C::NI], v_voff;
+    copy_offsets<D>(wave, lane, k_voff, v_voff);
 
     // LDS offsets this lane reads: K row tau(col), granules (2 kk + h) ^ key
     int k_off[4];
@@ -518,10 +524,21 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     };
 
     // ---- prologue: K(0), V(0), K(1); scores and softmax of tile 0 ----------------
+    // ok0, ok1: page offsets of the latest K tile copied, which the V copy
+    // of the next step reuses
+    int64_t ok0 = 0, ok1 = 0;
     if (n_tiles > 0) {
-        copy_k(0);
-        copy_v(0);
-        if (n_tiles > 1) copy_k(1);
+        const int64_t o0 = page_off(page_id(0)), o1 = page_off(page_id(1));
+        copy_k_run<D>(k_src + o0, k_voff, kslot(0), 0, wave);
+        copy_k_run<D>(k_src + o1, k_voff, kslot(0), 1, wave);
+        copy_v_run<D>(v_src + o0, v_voff, vslot(0), 0, wave);
+        copy_v_run<D>(v_src + o1, v_voff, vslot(0), 1, wave);
+        if (n_tiles > 1) {
+            ok0 = page_off(page_id(2));
+            ok1 = page_off(page_id(3));
+            copy_k_run<D>(k_src + ok0, k_voff, kslot(1), 0, wave);
+            copy_k_run<D>(k_src + ok1, k_voff, kslot(1), 1, wave);
+        }
         wait_vm<0>();
         lds_barrier();
         if (wave_live) {
@@ -546,16 +563,22 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         wait_vm<0>();              // V(t) and K(t+1), copied during the previous step
         lds_barrier();             // ... for every wave; and K(t), V(t-1) are no longer read
         // copies of this step: V(t+1) into V(t-1)'s slot, K(t+2) into K(t)'s
-        slide_ids(2 * (t + 1));
-        const int32_t pv0 = page_id(2 * t + 2), pv1 = page_id(2 * t + 3);
+        const int64_t ov0 = ok0, ov1 = ok1;        // V(t+1): the pages of K(t+1)
         const bool k_next = t + 2 < n_tiles;
-        const int32_t pk0 = k_next ? page_id(2 * t + 4) : 0, pk1 = k_next ? page_id(2 * t + 5) : 0;
+        if (k_next) {
+            slide_ids(2 * t + 4);
+            ok0 = page_off(page_id(2 * t + 4));
+            ok1 = page_off(page_id(2 * t + 5));
+        }
         const uint32_t vs = vslot(t + 1), ks = kslot(t + 2);
+        // run j of this step's copies: V(t+1) pages 0, 1, then K(t+2) pages 0, 1
         auto copy = [&](int j) {
-            if (j < C::DMA) issue_v_part<D>(a, vs, pv0, pv1, g, wave, lane, j);
-            else issue_k_part<D>(a, ks, pk0, pk1, g, wave, lane, j - C::DMA);
+            if (j == 0) copy_v_run<D>(v_src + ov0, v_voff, vs, 0, wave);
+            else if (j == 1) copy_v_run<D>(v_src + ov1, v_voff, vs, 1, wave);
+            else if (j == 2) copy_k_run<D>(k_src + ok0, k_voff, ks, 0, wave);
+            else copy_k_run<D>(k_src + ok1, k_voff, ks, 1, wave);
         };
-        const int n_copies = k_next ? 2 * C::DMA : C::DMA;
+        const int n_copies = k_next ? 4 : 2;
         zero_v_edges(t);
         if (wave_live) {
             const uint8_t* kbuf = lds + ((t + 1) & 1) * C::HALF;
