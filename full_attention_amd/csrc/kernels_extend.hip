@@ -239,66 +239,92 @@ __device__ __forceinline__ void copy_v_run(const uint8_t* src, uint32_t v_voff, 
     else dma16_s_x2(src, v_voff, v_voff, dst);
 }
 
-// Online softmax of one score tile s (lane: query row col, kv tokens
-// 8h..8h+7 and 16+8h..16+8h+7 of the tile at t0), masked where needed; returns
-// the two B operands of the value product (P^T, bf16) and updates the
-// running max / sum.  `rescale` is called with the factor for O when the
-// running max is raised.
-template <typename Rescale>
-__device__ __forceinline__ void softmax_tile(f32x16& s, int32_t t0, bool whole, int32_t row_lo, int32_t row_hi,
-                                             int h, float score_scale, float& m_run, float& l_run, u32x4 (&pb)[2],
-                                             Rescale rescale) {
-    if (!whole) {
-        // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
-        const int32_t lo_l = row_lo - t0 - 8 * h, hi_l = row_hi - t0 - 8 * h;
+// Online softmax of one score tile, in stages that the step spreads over its
+// value MFMAs (lane: query row col; s holds the row's scores of kv tokens
+// 8h..8h+7 and 16+8h..16+8h+7 of the tile at t0).  Stage 0 masks the tile
+// where it is not visible to every row and takes the max of the first eight
+// scores; stage 1 finishes the max and updates the running max, raised only
+// when the tile's max passes it by more than 2^8 (the factor `al` for O and
+// the wave-wide flag `raise` are left for the caller, which scales O before
+// the next value product); stages 2-5 exponentiate four scores each into s
+// and add them to the row sum; stage 6 packs the first kv half into pb0.  The
+// second half is packed by softmax_pack_hi once the value MFMAs of the
+// current tile no longer read pb1.
+struct SoftRow {
+    float mx;
+    float m_use;
+    float al;
+    bool raise;
+};
+
+__device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, int32_t t0, bool whole,
+                                              int32_t row_lo, int32_t row_hi, int h, float score_scale,
+                                              float& m_run, float& l_run, u32x4& pb0) {
+    if (stage == 0) {
+        if (!whole) {
+            // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
+            const int32_t lo_l = row_lo - t0 - 8 * h, hi_l = row_hi - t0 - 8 * h;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = e + ((e >> 3) << 3);
-            s[e] = ((c >= lo_l) & (c <= hi_l)) ? s[e] : -INFINITY;
+            for (int e = 0; e < 16; ++e) {
+                const int c = e + ((e >> 3) << 3);
+                s[e] = ((c >= lo_l) & (c <= hi_l)) ? s[e] : -INFINITY;
+            }
         }
-    }
-    float mx = s[0];
+        r.mx = s[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    mx = max_halves(mx) * score_scale;
-    const bool raise = mx > m_run + kRescale;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        for (int e = 1; e < 8; ++e) r.mx = fmaxf(r.mx, s[e]);
+    } else if (stage == 1) {
+        float mx = r.mx;
+#pragma unroll
+        for (int e = 8; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = max_halves(mx) * score_scale;
+        const bool raise = mx > m_run + kRescale;
+        r.raise = __builtin_amdgcn_ballot_w64(raise) != 0;
         const float m_new = raise ? mx : m_run;
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float al = raise ? alpha : 1.f;
-        l_run *= al;
+        r.al = raise ? alpha : 1.f;
+        l_run *= r.al;
         m_run = m_new;
-        rescale(al);
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        r.m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    } else if (stage <= 5) {
+        const int e0 = 4 * (stage - 2);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], score_scale, -m_use));
-        l_run += s[e];
+        for (int e = e0; e < e0 + 4; ++e) {
+            s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], score_scale, -r.m_use));
+            l_run += s[e];
+        }
+    } else if (stage == 6) {
+        pb0 = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]), cvt_pk_bf16(s[4], s[5]),
+                    cvt_pk_bf16(s[6], s[7])};
     }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-        pb[st] = u32x4{cvt_pk_bf16(s[8 * st + 0], s[8 * st + 1]), cvt_pk_bf16(s[8 * st + 2], s[8 * st + 3]),
-                       cvt_pk_bf16(s[8 * st + 4], s[8 * st + 5]), cvt_pk_bf16(s[8 * st + 6], s[8 * st + 7])};
+}
+constexpr int kSoftStages = 7;
+__device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1) {
+    pb1 = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]), cvt_pk_bf16(s[12], s[13]),
+                cvt_pk_bf16(s[14], s[15])};
 }
 
 // One wavefront's step of the software pipeline: the score product of tile
-// t+1 (kb) and the value product of tile t (vb, operands pb) interleaved, so
-// the independent MFMA chains keep the matrix core busy.  Each K or V operand
-// read from LDS feeds the MFMAs of all NRB row blocks of the wavefront.  The
-// LDS operands are prefetched PF steps ahead in rotating registers, and a
-// scheduling barrier closes every step so the compiler keeps this order (and
-// this register footprint) instead of hoisting every load.  copy(j) issues
-// run j (of at most kRuns) of the next tiles' global -> LDS copies, one run
-// every kRunGap steps of the loop, so the copies overlap the matrix work
-// instead of stalling every wavefront at the top of the step.  With
-// HAVE_S = false only the value product runs (the last tile).
-template <int D, bool HAVE_S, typename Copy>
+// t+1 (kb) and the value product of tile t (vb, operands pb), two independent
+// MFMA chains.  Step i of the loop issues value MFMA i and, in the first half,
+// score MFMAs 2i and 2i+1, so the scores are complete halfway through; the
+// second half runs soft(k), the stages of the softmax of tile t+1, between
+// the remaining value MFMAs, and soft_end() packs what the value MFMAs read
+// last.  Each K or V operand read from LDS feeds the MFMAs of all NRB row
+// blocks of the wavefront.  The LDS operands are prefetched a few steps
+// ahead in rotating registers, and a scheduling barrier closes every step so
+// the compiler keeps this order (and this register footprint) instead of
+// hoisting every load.  copy(j) issues run j (of at most kRuns) of the next
+// tiles' global -> LDS copies, one run every kRunGap steps of the loop, so the
+// copies overlap the matrix work instead of stalling every wavefront at the
+// top of the step.  With HAVE_S = false only the value product runs (the
+// last tile).
+template <int D, bool HAVE_S, typename Copy, typename Soft, typename SoftEnd>
 __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[4], int v_off,
                                           const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
                                           const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
-                                          f32x16 (&o)[16], int n_copies, Copy copy) {
-    constexpr int KK = D / 16, MT = D / 32, PF = 4, NRB = XCfg<D>::NRB;
+                                          f32x16 (&o)[16], int n_copies, Copy copy, Soft soft, SoftEnd soft_end) {
+    constexpr int KK = D / 16, MT = D / 32, H = KK / 2, PFK = 4, PFV = 4, NRB = XCfg<D>::NRB;
     constexpr int kRunGap = kRunGapSet > 0 ? kRunGapSet : KK / kRuns;
     static_assert((kRuns - 1) * kRunGap < KK, "every copy run needs a loop step");
     auto ld_k = [&](int i) { return *reinterpret_cast<const u32x4*>(kb + k_off[i & 3] + (i >> 2) * 128); };
@@ -306,36 +332,47 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
     auto ld_v = [&](int i) {
         return *reinterpret_cast<const u32x4*>(vb + (i / MT) * (16 * D * 2) + (i % MT) * 1024 + v_off);
     };
-    u32x4 kr[PF], vr[PF];
+    u32x4 kr[PFK], vr[PFV];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        vr[p] = ld_v(p);
-        if constexpr (HAVE_S) kr[p] = ld_k(p);
+    for (int p = 0; p < PFV; ++p) vr[p] = ld_v(p);
+    if constexpr (HAVE_S) {
+#pragma unroll
+        for (int p = 0; p < PFK; ++p) kr[p] = ld_k(p);
     }
 #pragma unroll
     for (int i = 0; i < KK; ++i) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             if (i == 0) asm_mfma_agpr_nop(o[rb * MT], vr[0], pb[rb][0]);
-            else asm_mfma_agpr(o[rb * MT + i % MT], vr[i % PF], pb[rb][i / MT]);
-            if constexpr (HAVE_S) {
-                if (i == 0) s[rb] = asm_mfma_first(kr[0], qreg[rb][0]);
-                else asm_mfma_acc(s[rb], kr[i % PF], qreg[rb][i]);
-            }
+            else asm_mfma_agpr(o[rb * MT + i % MT], vr[i % PFV], pb[rb][i / MT]);
         }
-        if (i + PF < KK) {
-            vr[i % PF] = ld_v(i + PF);
-            if constexpr (HAVE_S) kr[i % PF] = ld_k(i + PF);
+        if (i + PFV < KK) vr[i % PFV] = ld_v(i + PFV);
+        if constexpr (HAVE_S) {
+            if (i < H) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 2 * i + jj;
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        if (j == 0) s[rb] = asm_mfma_first(kr[0], qreg[rb][0]);
+                        else asm_mfma_acc(s[rb], kr[j % PFK], qreg[rb][j]);
+                    }
+                    if (j + PFK < KK) kr[j % PFK] = ld_k(j + PFK);
+                }
+                if (i == H - 1) {
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) asm_mfma_drain(s[rb]);
+                }
+            } else {
+                soft(i - H);
+            }
         }
         if (i % kRunGap == 0 && i / kRunGap < kRuns) {
             if (i / kRunGap < n_copies) copy(i / kRunGap);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (HAVE_S) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) asm_mfma_drain(s[rb]);
-    }
+    if constexpr (HAVE_S) soft_end();
 }
 
 template <int D>
@@ -484,19 +521,37 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     auto is_whole = [&](int32_t t0, int rb) -> bool {
         return (t0 + kTile - 1 <= min(w_pmin[rb], hi - 1)) && (a.window == 0 || w_pmax[rb] - a.window + 1 <= t0);
     };
-    // softmax of tile t0 for every row block; a rescale of row block rb's O
-    // first lets every value MFMA that wrote it land (settle_tiles)
+    // softmax state per row block; stage k of the softmax of tile t0 for
+    // every row block, spread (kSoftGap loop steps apart) over the second
+    // half of a step
     f32x16 s[NRB];
     u32x4 pb[NRB][2];
-    auto softmax_all = [&](int32_t t0) {
+    SoftRow sr[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) sr[rb].raise = false;
+    auto soft_stage_all = [&](int stage, int32_t t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            softmax_stage(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], h, a.score_scale,
+                          m_run[rb], l_run[rb], pb[rb][0]);
+    };
+    auto soft_pack_hi = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) softmax_pack_hi(s[rb], pb[rb][1]);
+    };
+    constexpr int kSoftGap = (C::KK / 2) / 8 > 0 ? (C::KK / 2) / 8 : 1;
+    static_assert(kSoftGap * (kSoftStages - 1) < C::KK / 2, "softmax stages must fit the second half of a step");
+    // O of row block rb times the factor its softmax left, once the value
+    // MFMAs that wrote O have landed; before the next value product
+    auto apply_rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            softmax_tile(s[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], h, a.score_scale, m_run[rb],
-                         l_run[rb], pb[rb], [&](float al) {
-                             settle_tiles(o);
+            if (sr[rb].raise) {
+                settle_tiles(o);
 #pragma unroll
-                             for (int m = 0; m < C::MT; ++m) agpr_scale(o[rb * C::MT + m], al);
-                         });
+                for (int m = 0; m < C::MT; ++m) agpr_scale(o[rb * C::MT + m], sr[rb].al);
+                sr[rb].raise = false;
+            }
         }
     };
     // zeroes V of tokens outside [lo, hi) in V tile t: never-written slots may hold NaN
@@ -552,7 +607,11 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
                                  qreg[rb][kk]);
                 asm_mfma_drain(s[rb]);
             }
-            softmax_all(t_begin);
+#pragma unroll
+            for (int st = 0; st < kSoftStages; ++st) soft_stage_all(st, t_begin);
+            soft_pack_hi();
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) sr[rb].raise = false;   // O is still zero
         }
     }
 
@@ -583,8 +642,14 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         if (wave_live) {
             const uint8_t* kbuf = lds + ((t + 1) & 1) * C::HALF;
             const uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
-            step_mfma<D, true>(kbuf, vbuf, k_off, v_off, qreg, pb, s, o, n_copies, copy);
-            softmax_all(t_begin + (t + 1) * kTile);
+            const int32_t t_next = t_begin + (t + 1) * kTile;
+            apply_rescale();
+            step_mfma<D, true>(
+                kbuf, vbuf, k_off, v_off, qreg, pb, s, o, n_copies, copy,
+                [&](int k) {
+                    if (k % kSoftGap == 0 && k / kSoftGap < kSoftStages) soft_stage_all(k / kSoftGap, t_next);
+                },
+                soft_pack_hi);
         } else {
             for (int j = 0; j < n_copies; ++j) copy(j);     // a wavefront with no rows still copies its share
         }
@@ -598,7 +663,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         zero_v_edges(t);
         if (wave_live) {
             const uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
-            step_mfma<D, false>(lds, vbuf, k_off, v_off, qreg, pb, s, o, 0, [](int) {});
+            apply_rescale();
+            step_mfma<D, false>(lds, vbuf, k_off, v_off, qreg, pb, s, o, 0, [](int) {}, [](int) {}, []() {});
         }
         settle_tiles(o);   // the last value MFMAs have landed before the output reads them
     }
