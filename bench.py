@@ -154,18 +154,32 @@ def setup_decode(torch):
     st = dict(wl=wl, cache=cache, layers=layers, owners=owners, B=B, L=L, kv_len=kv_len,
               cu_new=i32(torch, np.arange(B + 1)), pos_new=i32(torch, L), kv_len_t=i32(torch, kv_len),
               max_kv_len=int(kv_len.max()), new_k=new_k, new_v=new_v, q=q, out=out, pool=pool)
-    # one workspace big enough for every layer, allocated before any capture
+    # one workspace big enough for every layer, and one plan buffer per kind of
+    # layer, allocated before any capture
     need = max(cache.workspace(l, B, st["max_kv_len"])[1] for l in range(len(layers)))
     cache._workspace = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    st["plans"] = {}
+    for l in range(len(layers)):
+        key = cache.plan_key(l)
+        if key not in st["plans"]:
+            st["plans"][key] = (l, cache.decode_plan(l, st["kv_len_t"], st["max_kv_len"]))
     return st
 
 
 def decode_step(st):
+    """Store the new token's K/V on the owners and decode every layer.  The
+    split of the keys is planned once per step for each kind of layer (window,
+    Hkv) and shared by all layers of that kind."""
+    from full_attention_amd import pakv as pakv_mod
     cache = st["cache"]
+    for key, (layer, buf) in st["plans"].items():
+        pakv_mod.decode_plan(cache.map, layer, cache.pages, st["kv_len_t"], st["B"], st["max_kv_len"],
+                             buf, buf.numel())
     for l in range(len(st["layers"])):
         if l in st["new_k"]:
             cache.store(l, st["cu_new"], st["pos_new"], st["new_k"][l], st["new_v"][l])
-        cache.decode(l, st["kv_len_t"], st["q"][l], st["max_kv_len"], out=st["out"][l])
+        plan = st["plans"][cache.plan_key(l)][1]
+        cache.decode(l, st["kv_len_t"], st["q"][l], st["max_kv_len"], out=st["out"][l], plan=plan)
 
 
 def decode_bytes(st):

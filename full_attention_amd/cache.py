@@ -80,13 +80,34 @@ class PagedKVCache:
             self._workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._workspace, need
 
-    def decode(self, layer, kv_lens, q, max_kv_len, out=None, stream=None):
+    def plan_key(self, layer):
+        """Layers with equal keys can share a decode plan (same window and Hkv)."""
+        s = self.specs[layer]
+        return (s["window"], s["num_kv_heads"])
+
+    def decode_plan(self, layer, kv_lens, max_kv_len, stream=None):
+        """The split of a decode call's keys for layer's window and Hkv, as a
+        device buffer; valid for every layer with the same plan_key while
+        kv_lens and the page table stay unchanged."""
+        nseq = kv_lens.shape[0]
+        nbytes = pakv.decode_plan_bytes(self.map, layer, nseq, max_kv_len)
+        plan = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        pakv.decode_plan(self.map, layer, self.pages, kv_lens, nseq, max_kv_len, plan, plan.numel(), stream)
+        return plan
+
+    def decode(self, layer, kv_lens, q, max_kv_len, out=None, stream=None, plan=None):
+        """plan: a buffer from decode_plan for a layer with the same plan_key
+        (kv_lens is then not read), or None."""
         nseq = q.shape[0]
         if out is None:
             out = torch.empty_like(q)
         ws, need = self.workspace(layer, nseq, max_kv_len)
-        pakv.paged_attn_decode(self.map, layer, self.pages, kv_lens, q, out, nseq, max_kv_len,
-                               ws, ws.numel(), stream)
+        if plan is None:
+            pakv.paged_attn_decode(self.map, layer, self.pages, kv_lens, q, out, nseq, max_kv_len,
+                                   ws, ws.numel(), stream)
+        else:
+            pakv.paged_attn_decode_planned(self.map, layer, self.pages, plan, plan.numel(), q, out, nseq,
+                                           max_kv_len, ws, ws.numel(), stream)
         return out
 
     def extend(self, layer, cu_q, prefix_lens, q, max_q_len, max_kv_len, out=None, stream=None):

@@ -67,6 +67,8 @@ struct DecodeArgs {
     float score_scale;      // sm_scale * log2(e)
     int32_t max_kv_len;
     int32_t grid;           // workgroups
+    int32_t* sched;         // schedule buffer (word offsets below)
+    int64_t s_soff, s_slen, s_rec, s_ids, s_cap;
     uint32_t* arrivals;     // [U] partials written per unit; zero between calls
     float* part_o;          // [grid + U][G][D]
     float* part_ml;         // [grid + U][G][2]
@@ -184,22 +186,75 @@ __device__ __forceinline__ void build_seq_table(const DecodeArgs& a, const int32
     __syncthreads();
 }
 
-// Page ids of stream chunks c0 .. c0 + 63 (lane j holds chunk c0 + j; lanes
-// past `count` hold 0).  Ids outside the pool become 0, so a bad table never
-// makes a copy leave the slab.
-__device__ __forceinline__ uint32_t load_ids(const DecodeArgs& a, const int32_t* __restrict__ page_table,
-                                             const SeqTable& st, int32_t B, int32_t c0, int32_t count, int lane) {
-    uint32_t id = 0;
-    if (lane < count) {
-        const int32_t c = c0 + lane;
-        const int32_t b = seq_of_chunk(st, B, c);
-        const int32_t len = st.slen[b];
-        const int32_t n = chunks_of(a, len);
-        const int32_t k = (c - st.soff[b]) % n;
-        const int32_t ph = page_table[(int64_t)b * a.max_pages + (window_lo(a, len) >> 4) + k];
-        id = ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : 0u;
+// Page id of stream chunk c: the page of sequence b holding the chunk's 16
+// keys.  Ids outside the pool become 0, so a bad table never makes a copy
+// leave the slab.
+__device__ __forceinline__ uint32_t page_of_chunk(const DecodeArgs& a, const int32_t* __restrict__ page_table,
+                                                  const SeqTable& st, int32_t B, int32_t c) {
+    const int32_t b = seq_of_chunk(st, B, c);
+    const int32_t len = st.slen[b];
+    const int32_t n = chunks_of(a, len);
+    const int32_t k = (c - st.soff[b]) % n;
+    const int32_t ph = page_table[(int64_t)b * a.max_pages + (window_lo(a, len) >> 4) + k];
+    return ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : 0u;
+}
+
+// The schedule of a decode call (the plan): every workgroup of the plan
+// kernel builds the sequence table, takes the run of the chunk stream that
+// decode workgroup blockIdx.x will take (equal contiguous runs of
+// ceil(T / grid) chunks) and writes its record and the page ids of its
+// chunks; workgroup 0 also writes the header and the table.
+__global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
+                                                           const int32_t* __restrict__ kv_lens) {
+    __shared__ int32_t seq_lds[2 * (pakv::kDecodeMaxSeqs + 1)];
+    const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
+    const int t = threadIdx.x;
+    const int32_t B = a.num_seqs;
+    build_seq_table(a, kv_lens, st, B);
+    const int32_t T = st.soff[B];
+    const int32_t per = (T + a.grid - 1) / a.grid;
+    const int32_t c_begin = min((int32_t)blockIdx.x * per, T);
+    const int32_t c_end = min(c_begin + per, T);
+    int32_t* S = a.sched;
+    if (blockIdx.x == 0) {
+        if (t == 0) {
+            const int32_t head[8] = {pakv::kPlanMagic, T, per, a.grid, B, a.hkv, a.window, a.max_kv_len};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) S[i] = head[i];
+        }
+        for (int i = t; i <= B; i += 256) S[a.s_soff + i] = st.soff[i];
+        for (int i = t; i < B; i += 256) S[a.s_slen + i] = st.slen[i];
     }
-    return id;
+    int32_t* rec = S + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
+    if (t == 0) {
+        int32_t u = 0, kc = 0;
+        if (c_begin < c_end) {
+            const int32_t b = seq_of_chunk(st, B, c_begin);
+            const int32_t n = chunks_of(a, st.slen[b]);
+            const int32_t r = c_begin - st.soff[b];
+            u = b * a.hkv + r / n;
+            kc = r % n;
+        }
+        rec[0] = c_begin;
+        rec[1] = c_end;
+        rec[2] = u;
+        rec[3] = kc;
+        rec[4] = per;
+    }
+    for (int32_t j = t; j < max(c_end - c_begin, 64); j += 256) {
+        const bool in_run = c_begin + j < c_end;
+        const uint32_t id = in_run ? page_of_chunk(a, page_table, st, B, c_begin + j) : 0u;
+        if (j < 64) rec[pakv::kPlanRecIds + j] = (int32_t)id;
+        if (in_run) S[a.s_ids + c_begin + j] = (int32_t)id;
+    }
+}
+
+// Page ids of stream chunks c0 .. c0 + count - 1 from the schedule (lane j
+// holds chunk c0 + j; lanes past `count` hold 0), re-clamped to the pool.
+__device__ __forceinline__ uint32_t sched_ids(const DecodeArgs& a, int32_t c0, int32_t count, int lane) {
+    uint32_t id = 0;
+    if (lane < count && c0 + lane < a.s_cap) id = (uint32_t)a.sched[a.s_ids + c0 + lane];
+    return (id < (uint32_t)a.num_pages) ? id : 0u;
 }
 
 // Q^T operand of a wave's dim quarter: column `col` = head g*G + col (zero
@@ -364,8 +419,7 @@ __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32
 }
 
 template <int D, bool INT8>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
-                                                         const int32_t* __restrict__ kv_lens) {
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     using C = Cfg<D, INT8>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     __shared__ uint32_t ticket;
@@ -380,32 +434,40 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
     const int32_t B = a.num_seqs;
     const int32_t U = B * a.hkv;
 
-    build_seq_table(a, kv_lens, st, B);
-    const int32_t T = st.soff[B];
-    const int32_t per = (T + a.grid - 1) / a.grid;
-    const int32_t c_begin = blockIdx.x * per;
-    const int32_t c_end = min(c_begin + per, T);
+    // the schedule: the sequence table into LDS, this workgroup's record and
+    // the page ids of its first 64 chunks, all loads issued before any wait
+    // (one round trip); then Q of the first unit and the first chunks' copies
+    // (a second round trip, awaited with the first chunk)
+    const int32_t* rec = a.sched + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
+    int32_t tab_o[4], tab_l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {        // B <= 1023: at most four entries per thread
+        const int i = threadIdx.x + 256 * k;
+        tab_o[k] = (i <= B) ? a.sched[a.s_soff + i] : 0;
+        tab_l[k] = (i < B) ? a.sched[a.s_slen + i] : 1;
+    }
+    const int32_t field = rec[min(lane, 7)];
+    uint32_t ids = (uint32_t)rec[pakv::kPlanRecIds + lane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        if (i <= B) st.soff[i] = tab_o[k];
+        if (i < B) st.slen[i] = clamp_i32(tab_l[k], 1, a.max_kv_len);
+    }
+    const int32_t c_begin = max(__builtin_amdgcn_readlane(field, 0), 0);
+    const int32_t c_end = (int32_t)min((int64_t)__builtin_amdgcn_readlane(field, 1), a.s_cap);
+    const int32_t u_first = clamp_i32(__builtin_amdgcn_readlane(field, 2), 0, U - 1);
+    const int32_t kc_first = max(__builtin_amdgcn_readlane(field, 3), 0);
+    const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 1);
+    ids = (ids < (uint32_t)a.num_pages) ? ids : 0u;
+    __syncthreads();
     if (c_begin >= c_end) return;
     const int32_t total = c_end - c_begin;
 
-    // first unit of the run, and the page ids of its first 64 chunks (with Q:
-    // one round trip before the first copy)
-    Unit uc;
-    int32_t kc;
-    {
-        const int32_t b = seq_of_chunk(st, B, c_begin);
-        const int32_t n = chunks_of(a, st.slen[b]);
-        const int32_t r = c_begin - st.soff[b];
-        uc = unit_of(a, st, b * a.hkv + r / n);
-        kc = r % n;
-    }
+    Unit uc = unit_of(a, st, u_first);
+    int32_t kc = min(kc_first, uc.n - 1);
     Unit ui = uc;                                 // issue cursor
     int32_t ki = kc;
-    uint32_t ids = load_ids(a, page_table, st, B, c_begin, min(total, 64), lane);
-    const int dq = wave * (D / 4);
-    u32x4 qreg[C::KK];
-    load_q<D>(a, uc, G, col, qg, dq, qreg);
-    wait_vm<0>();   // ids and Q have landed; nothing the compiler issued stays in flight
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
@@ -413,6 +475,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
             advance(a, st, U, ui, ki);
         }
     }
+    const int dq = wave * (D / 4);
+    u32x4 qreg[C::KK];
+    load_q<D>(a, uc, G, col, qg, dq, qreg);
 
     f32x4 o[C::MT];
 #pragma unroll
@@ -440,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
             const int32_t j = i + C::NBUF - 1;        // chunk to copy now
             if (j < total) {
                 if ((j & 63) == 0) {                  // next window of page ids (drains, once per 64)
-                    ids = load_ids(a, page_table, st, B, c_begin + j, min(total - j, 64), lane);
+                    ids = sched_ids(a, c_begin + j, min(total - j, 64), lane);
                     wait_vm<0>();
                 }
                 issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, j & 63),
@@ -580,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a, const int3
 
 namespace pakv {
 
-int launch_decode(const DecodeLaunch& s, void* stream) {
+static DecodeArgs args_of(const DecodeLaunch& s) {
     DecodeArgs a;
     a.k_slab = static_cast<const uint8_t*>(s.slab.k);
     a.v_slab = static_cast<const uint8_t*>(s.slab.v);
@@ -598,19 +663,37 @@ int launch_decode(const DecodeLaunch& s, void* stream) {
     a.score_scale = s.sm_scale * kLog2e;
     a.max_kv_len = s.max_kv_len;
     a.grid = s.plan.grid;
+    a.sched = s.sched;
+    a.s_soff = s.layout.soff;
+    a.s_slen = s.layout.slen;
+    a.s_rec = s.layout.rec;
+    a.s_ids = s.layout.ids;
+    a.s_cap = s.layout.cap;
     a.arrivals = s.arrivals;
     a.part_o = s.part_o;
     a.part_ml = s.part_ml;
+    return a;
+}
+
+int launch_decode_plan(const DecodeLaunch& s, void* stream) {
+    const DecodeArgs a = args_of(s);
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(s.plan.grid), dim3(256), 0, static_cast<hipStream_t>(stream), a,
+                       s.page_table, s.kv_lens);
+    return (int)hipGetLastError();
+}
+
+int launch_decode(const DecodeLaunch& s, void* stream) {
+    const DecodeArgs a = args_of(s);
     hipStream_t st = static_cast<hipStream_t>(stream);
     dim3 grid1(s.plan.grid);
     const bool i8 = s.kv_dtype == PAKV_KV_INT8_PTH;
     const int K = PAKV_TIME_DECODE;
     if (s.head_dim == 256) {
-        if (i8) launch(K, decode_kernel<256, true>, grid1, dim3(256), 0, st, a, s.page_table, s.kv_lens);
-        else launch(K, decode_kernel<256, false>, grid1, dim3(256), 0, st, a, s.page_table, s.kv_lens);
+        if (i8) launch(K, decode_kernel<256, true>, grid1, dim3(256), 0, st, a);
+        else launch(K, decode_kernel<256, false>, grid1, dim3(256), 0, st, a);
     } else {
-        if (i8) launch(K, decode_kernel<512, true>, grid1, dim3(256), 0, st, a, s.page_table, s.kv_lens);
-        else launch(K, decode_kernel<512, false>, grid1, dim3(256), 0, st, a, s.page_table, s.kv_lens);
+        if (i8) launch(K, decode_kernel<512, true>, grid1, dim3(256), 0, st, a);
+        else launch(K, decode_kernel<512, false>, grid1, dim3(256), 0, st, a);
     }
     return (int)hipGetLastError();
 }

@@ -54,11 +54,30 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs) {
 // partial o, then partial (m, l); 256-byte aligned parts.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs) {
+size_t decode_partial_bytes(const pakv_layer_desc& d, int32_t num_seqs) {
     DecodePlan p = plan_decode(d, num_seqs);
     size_t slots = (size_t)(p.grid + p.units) * p.group;
     return align256((size_t)kDecodeMaxUnits * sizeof(uint32_t)) + align256(slots * d.head_dim * sizeof(float)) +
-           slots * 2 * sizeof(float);
+           align256(slots * 2 * sizeof(float));
+}
+
+PlanLayout plan_layout(int32_t num_seqs, int32_t hkv, int32_t max_kv_len) {
+    PlanLayout l;
+    l.soff = kPlanHeader;
+    l.slen = l.soff + num_seqs + 1;
+    l.rec = (l.slen + num_seqs + 15) & ~(int64_t)15;
+    l.ids = l.rec + (int64_t)kDecodeGrid * kPlanRecord;
+    l.cap = (int64_t)num_seqs * hkv * ((max_kv_len + 15) / 16);
+    l.words = l.ids + l.cap;
+    return l;
+}
+
+size_t decode_plan_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len) {
+    return align256((size_t)plan_layout(num_seqs, d.num_kv_heads, max_kv_len).words * sizeof(int32_t));
+}
+
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len) {
+    return decode_partial_bytes(d, num_seqs) + decode_plan_bytes(d, num_seqs, max_kv_len);
 }
 
 static bool layer_ok(const pakv_layer_map* m, int32_t layer) {
@@ -269,23 +288,25 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
 size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
                                    int32_t num_seqs, int32_t max_kv_len) {
     if (!layer_ok(map, layer) || num_seqs < 0 || max_kv_len < 1) return 0;
-    return decode_workspace_bytes(map->layers[layer].desc, num_seqs);
+    return decode_workspace_bytes(map->layers[layer].desc, num_seqs, max_kv_len);
 }
 
-pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
-                                   const int32_t* kv_lens, const void* q, void* out,
-                                   int32_t num_seqs, int32_t max_kv_len,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
-    clear_error();
+size_t pakv_decode_plan_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_kv_len) {
+    if (!layer_ok(map, layer) || num_seqs < 0 || max_kv_len < 1) return 0;
+    return decode_plan_bytes(map->layers[layer].desc, num_seqs, max_kv_len);
+}
+
+// Checks shared by the decode calls and fills everything but the buffers.
+static pakv_status decode_setup(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                int32_t num_seqs, int32_t max_kv_len, DecodeLaunch& a) {
     if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
     if (num_seqs < 0) return fail(PAKV_ERR_INVALID, "num_seqs < 0");
-    if (num_seqs == 0) return PAKV_OK;
     if (max_kv_len < 1) return fail(PAKV_ERR_INVALID, "max_kv_len must be at least 1");
+    if (num_seqs == 0) return PAKV_OK;
     if (pakv_status s = check_pages(pages, num_seqs)) return s;
     if ((int64_t)max_kv_len > (int64_t)pages->max_pages_per_seq * PAKV_PAGE_SIZE)
         return fail(PAKV_ERR_INVALID, "max_kv_len %d exceeds the page table's %d positions", max_kv_len,
                     pages->max_pages_per_seq * PAKV_PAGE_SIZE);
-    if (!kv_lens || !q || !out) return fail(PAKV_ERR_INVALID, "kv_lens, q or out is null");
     const auto& L = map->layers[layer];
     const auto& S = map->layers[L.source];
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
@@ -294,17 +315,10 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     if ((int64_t)num_seqs * L.desc.num_kv_heads > kDecodeMaxUnits)
         return fail(PAKV_ERR_UNSUPPORTED, "num_seqs * Hkv = %lld above %d per decode call",
                     (long long)num_seqs * L.desc.num_kv_heads, kDecodeMaxUnits);
-    size_t need = decode_workspace_bytes(L.desc, num_seqs);
-    if (!workspace || workspace_bytes < need)
-        return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    DecodeLaunch a;
+    a = DecodeLaunch{};
     a.slab = view_of(S);
     a.page_table = pages->page_table;
     a.max_pages = pages->max_pages_per_seq;
-    a.kv_lens = kv_lens;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = static_cast<uint16_t*>(out);
     a.num_seqs = num_seqs;
     a.max_kv_len = max_kv_len;
     a.hq = L.desc.num_q_heads;
@@ -314,6 +328,14 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     a.kv_dtype = L.desc.kv_dtype;
     a.sm_scale = L.desc.sm_scale;
     a.plan = plan_decode(L.desc, num_seqs);
+    a.layout = plan_layout(num_seqs, a.hkv, max_kv_len);
+    return PAKV_OK;
+}
+
+// Workspace: arrival counters (a fixed region of kDecodeMaxUnits, so that
+// layers of any shape can share one workspace and leave it zeroed), partial o,
+// partial (m, l); then, for the unplanned call, its schedule.
+static void bind_partials(DecodeLaunch& a, void* workspace) {
     size_t slots = (size_t)(a.plan.grid + a.plan.units) * a.plan.group;
     char* ws = static_cast<char*>(workspace);
     a.arrivals = reinterpret_cast<uint32_t*>(ws);
@@ -321,6 +343,69 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     a.part_o = reinterpret_cast<float*>(ws);
     ws += align256(slots * a.head_dim * sizeof(float));
     a.part_ml = reinterpret_cast<float*>(ws);
+}
+
+pakv_status pakv_decode_plan(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                             const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                             void* plan, size_t plan_bytes, void* stream) {
+    clear_error();
+    DecodeLaunch a;
+    if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
+    if (num_seqs == 0) return PAKV_OK;
+    if (!kv_lens) return fail(PAKV_ERR_INVALID, "kv_lens is null");
+    size_t need = decode_plan_bytes(map->layers[layer].desc, num_seqs, max_kv_len);
+    if (!plan || plan_bytes < need)
+        return fail(PAKV_ERR_WORKSPACE, "decode plan needs %zu bytes, got %zu", need, plan ? plan_bytes : (size_t)0);
+    a.kv_lens = kv_lens;
+    a.sched = static_cast<int32_t*>(plan);
+    return hip_status(launch_decode_plan(a, stream), "decode_plan launch");
+}
+
+pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                           const void* plan, size_t plan_bytes, const void* q, void* out,
+                                           int32_t num_seqs, int32_t max_kv_len,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    DecodeLaunch a;
+    if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
+    if (num_seqs == 0) return PAKV_OK;
+    if (!q || !out) return fail(PAKV_ERR_INVALID, "q or out is null");
+    const auto& d = map->layers[layer].desc;
+    size_t need_plan = decode_plan_bytes(d, num_seqs, max_kv_len);
+    if (!plan || plan_bytes < need_plan)
+        return fail(PAKV_ERR_WORKSPACE, "decode plan needs %zu bytes, got %zu", need_plan,
+                    plan ? plan_bytes : (size_t)0);
+    size_t need = decode_partial_bytes(d, num_seqs);
+    if (!workspace || workspace_bytes < need)
+        return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.sched = const_cast<int32_t*>(static_cast<const int32_t*>(plan));
+    bind_partials(a, workspace);
+    return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
+}
+
+pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* kv_lens, const void* q, void* out,
+                                   int32_t num_seqs, int32_t max_kv_len,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    DecodeLaunch a;
+    if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
+    if (num_seqs == 0) return PAKV_OK;
+    if (!kv_lens || !q || !out) return fail(PAKV_ERR_INVALID, "kv_lens, q or out is null");
+    const auto& d = map->layers[layer].desc;
+    size_t need = decode_workspace_bytes(d, num_seqs, max_kv_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    a.kv_lens = kv_lens;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    bind_partials(a, workspace);
+    a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + decode_partial_bytes(d, num_seqs));
+    if (int e = launch_decode_plan(a, stream)) return hip_status(e, "decode_plan launch");
     return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
 }
 

@@ -35,7 +35,35 @@ struct DecodePlan {
     int32_t group;          // Hq / Hkv
 };
 DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
-size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs);
+
+// The schedule of a decode call (pakv_decode_plan), a device buffer of int32
+// words written by the plan kernel from kv_lens and the page table and read by
+// the decode kernel, so that a decode workgroup learns its run of the chunk
+// stream and the first page ids in one load:
+//   [0, kPlanHeader)   magic, total chunks T, chunks per workgroup, grid, B,
+//                      Hkv, window, max_kv_len
+//   soff [B + 1]       first stream chunk of each sequence's units; soff[B] = T
+//   slen [B]           length of each sequence, clamped to [1, max_kv_len]
+//   rec  [grid][kPlanRecord]  per workgroup: first chunk, end chunk, unit of
+//                      the first chunk, that chunk's index in its unit, chunks
+//                      per workgroup, spare words, then from word kPlanRecIds
+//                      the page ids of its first 64 chunks (0 past its run)
+//   ids  [cap]         page id of every stream chunk (ids outside the pool
+//                      already replaced by 0)
+constexpr int32_t kPlanMagic = 0x31504b50;
+constexpr int32_t kPlanHeader = 16;
+constexpr int32_t kPlanRecord = 80;
+constexpr int32_t kPlanRecIds = 16;
+struct PlanLayout {
+    int64_t soff, slen, rec, ids;   // word offsets
+    int64_t cap;                    // chunk capacity of ids
+    int64_t words;
+};
+PlanLayout plan_layout(int32_t num_seqs, int32_t hkv, int32_t max_kv_len);
+size_t decode_plan_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len);
+// partials and arrival counters; the unplanned call also keeps its plan there
+size_t decode_partial_bytes(const pakv_layer_desc& d, int32_t num_seqs);
+size_t decode_workspace_bytes(const pakv_layer_desc& d, int32_t num_seqs, int32_t max_kv_len);
 
 // ---- launchers (defined in the .hip translation units) ----------------------
 struct SlabView {
@@ -78,11 +106,14 @@ struct DecodeLaunch {
     int32_t kv_dtype;
     float sm_scale;
     DecodePlan plan;
+    int32_t* sched;     // the schedule buffer (written by the plan kernel, read by the decode kernel)
+    PlanLayout layout;
     uint32_t* arrivals; // [units], zero between calls
     float* part_o;      // [grid + units][G][D]
     float* part_ml;     // [grid + units][G][2]
 };
-int launch_decode(const DecodeLaunch& a, void* stream);
+int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
+int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched
 
 struct ExtendLaunch {
     SlabView slab;

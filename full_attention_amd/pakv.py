@@ -30,6 +30,7 @@ EXPORTED = (
     "pakv_last_error", "pakv_resolve_kv_sources", "pakv_layer_map_create", "pakv_layer_map_destroy",
     "pakv_layer_map_bind_slab", "pakv_layer_map_source", "pakv_kv_bytes_per_token", "pakv_slab_bytes",
     "pakv_paged_kv_store", "pakv_decode_workspace_bytes", "pakv_paged_attn_decode",
+    "pakv_decode_plan_bytes", "pakv_decode_plan", "pakv_paged_attn_decode_planned",
     "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used",
 )
 
@@ -80,6 +81,12 @@ lib.pakv_decode_workspace_bytes.restype = _S
 lib.pakv_decode_workspace_bytes.argtypes = [_P, _I, _I, _I]
 lib.pakv_paged_attn_decode.restype = _I
 lib.pakv_paged_attn_decode.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _I, _I, _P, _S, _P]
+lib.pakv_decode_plan_bytes.restype = _S
+lib.pakv_decode_plan_bytes.argtypes = [_P, _I, _I, _I]
+lib.pakv_decode_plan.restype = _I
+lib.pakv_decode_plan.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _I, _I, _P, _S, _P]
+lib.pakv_paged_attn_decode_planned.restype = _I
+lib.pakv_paged_attn_decode_planned.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _S, _P, _P, _I, _I, _P, _S, _P]
 lib.pakv_paged_attn_extend.restype = _I
 lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
 lib.pakv_set_timing_events.restype = _I
@@ -195,6 +202,22 @@ def paged_attn_decode(layer_map, layer, pages, kv_lens, q, out, num_seqs, max_kv
     return _check(lib.pakv_paged_attn_decode(layer_map.handle, layer, ctypes.byref(pages), _ptr(kv_lens),
                                              _ptr(q), _ptr(out), num_seqs, max_kv_len, _ptr(workspace),
                                              workspace_bytes, _stream(stream)))
+
+
+def decode_plan_bytes(layer_map, layer, num_seqs, max_kv_len):
+    return lib.pakv_decode_plan_bytes(layer_map.handle, layer, num_seqs, max_kv_len)
+
+
+def decode_plan(layer_map, layer, pages, kv_lens, num_seqs, max_kv_len, plan, plan_bytes, stream=None):
+    return _check(lib.pakv_decode_plan(layer_map.handle, layer, ctypes.byref(pages), _ptr(kv_lens), num_seqs,
+                                       max_kv_len, _ptr(plan), plan_bytes, _stream(stream)))
+
+
+def paged_attn_decode_planned(layer_map, layer, pages, plan, plan_bytes, q, out, num_seqs, max_kv_len,
+                              workspace, workspace_bytes, stream=None):
+    return _check(lib.pakv_paged_attn_decode_planned(layer_map.handle, layer, ctypes.byref(pages), _ptr(plan),
+                                                     plan_bytes, _ptr(q), _ptr(out), num_seqs, max_kv_len,
+                                                     _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_seqs, total_q, max_q_len,

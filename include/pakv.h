@@ -178,7 +178,8 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
                                 const void* k, const void* v,
                                 int32_t num_seqs, int32_t total_tokens, void* stream);
 
-/* Workspace bytes pakv_paged_attn_decode needs for these sizes. */
+/* Workspace bytes pakv_paged_attn_decode needs for these sizes (enough for
+ * pakv_paged_attn_decode_planned as well). */
 size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
                                    int32_t num_seqs, int32_t max_kv_len);
 
@@ -205,6 +206,28 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
                                    const int32_t* kv_lens, const void* q, void* out,
                                    int32_t num_seqs, int32_t max_kv_len,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode in two calls, for a step that decodes several layers over the same
+ * sequences: the split of the keys into workgroup runs and the page ids of
+ * every run depend only on kv_lens, the page table, the window and Hkv, so
+ * pakv_decode_plan computes them once into `plan` (device memory of at least
+ * pakv_decode_plan_bytes(...), owned by the caller; asynchronous on the
+ * stream) and pakv_paged_attn_decode_planned runs a layer's attention from it.
+ * A plan made for `layer` serves every layer with the same window and Hkv
+ * while kv_lens, the page table, num_seqs and max_kv_len stay as they were
+ * when it was made; the caller keeps to that (the kernel cannot tell, but
+ * re-clamps page ids to the slab, so a stale plan gives wrong values, never a
+ * read outside the slab).  The planned call takes the same arguments and
+ * workspace as pakv_paged_attn_decode, minus kv_lens, and gives bit-identical
+ * output. */
+size_t pakv_decode_plan_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_kv_len);
+pakv_status pakv_decode_plan(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                             const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                             void* plan, size_t plan_bytes, void* stream);
+pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                           const void* plan, size_t plan_bytes, const void* q, void* out,
+                                           int32_t num_seqs, int32_t max_kv_len,
+                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Chunked prefill: a chunk of new queries per sequence after a cached prefix.
  *   cu_q        : device int32 [num_seqs + 1], prefix sums of chunk lengths n_b

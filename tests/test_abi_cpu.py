@@ -181,12 +181,42 @@ def test_unbound_source_slab_is_an_error():
     assert st == pakv.ERR_INVALID and "not bound" in pakv.last_error()
 
 
-def test_workspace_depends_on_batch_not_context():
+def test_workspace_and_plan_sizes():
     m = pakv.LayerMap([_desc(d=512), _desc(d=256, w=512)])
-    a = pakv.decode_workspace_bytes(m, 0, 64, 4097)
-    assert a == pakv.decode_workspace_bytes(m, 0, 64, 131073)
-    assert 0 < pakv.decode_workspace_bytes(m, 0, 8, 4097) < a
-    assert pakv.decode_workspace_bytes(m, 1, 64, 4097) < a     # D 256 partials are half the size
+    p_short = pakv.decode_plan_bytes(m, 0, 64, 4097)
+    p_long = pakv.decode_plan_bytes(m, 0, 64, 131073)
+    # the plan holds a page id per 16 keys of every sequence
+    assert p_long - p_short >= 64 * ((131073 + 15) // 16 - (4097 + 15) // 16) * 4 - 256
+    # the partials (the rest of the workspace) depend on the batch, not the context
+    part = lambda layer, nseq, ctx: (pakv.decode_workspace_bytes(m, layer, nseq, ctx)
+                                     - pakv.decode_plan_bytes(m, layer, nseq, ctx))
+    assert part(0, 64, 4097) == part(0, 64, 131073) > 0
+    assert 0 < part(0, 8, 4097) < part(0, 64, 4097)
+    assert part(1, 64, 4097) < part(0, 64, 4097)     # D 256 partials are half the size
+    assert pakv.decode_plan_bytes(m, 0, 64, 0) == 0 and pakv.decode_plan_bytes(m, 5, 64, 10) == 0
+
+
+def test_plan_argument_errors_are_returned_before_launch():
+    m = _bound_map()
+    pages = pakv.Pages(0x5000, 2, 4)
+    lib = pakv.lib
+    need = lib.pakv_decode_plan_bytes(m.handle, 0, 2, 40)
+    assert need > 0
+    # plan: buffer too small, null kv_lens
+    assert lib.pakv_decode_plan(m.handle, 0, ctypes.byref(pages), 0x6000, 2, 40, 0x9000, need - 1,
+                                None) == pakv.ERR_WORKSPACE
+    assert lib.pakv_decode_plan(m.handle, 0, ctypes.byref(pages), None, 2, 40, 0x9000, need,
+                                None) == pakv.ERR_INVALID
+    # planned decode: missing plan, small workspace, null q
+    ws = lib.pakv_decode_workspace_bytes(m.handle, 0, 2, 40)
+    assert lib.pakv_paged_attn_decode_planned(m.handle, 0, ctypes.byref(pages), None, 0, 0x6100, 0x7000, 2, 40,
+                                              0x8000, ws, None) == pakv.ERR_WORKSPACE
+    assert lib.pakv_paged_attn_decode_planned(m.handle, 0, ctypes.byref(pages), 0x9000, need, 0x6100, 0x7000,
+                                              2, 40, 0x8000, 16, None) == pakv.ERR_WORKSPACE
+    assert lib.pakv_paged_attn_decode_planned(m.handle, 0, ctypes.byref(pages), 0x9000, need, None, 0x7000,
+                                              2, 40, 0x8000, ws, None) == pakv.ERR_INVALID
+    # no sequences -> nothing to do
+    assert lib.pakv_decode_plan(m.handle, 0, ctypes.byref(pages), None, 0, 40, None, 0, None) == pakv.OK
 
 
 def test_too_many_sequences_or_units_per_decode_call_are_refused():

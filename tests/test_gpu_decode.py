@@ -193,3 +193,78 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_planned_decode_matches_unplanned_bitwise(kv_dtype):
+    """One plan per (window, Hkv), shared by every layer of that kind, gives the
+    same bits as the one-call decode, including runs that cross units and
+    batches of page ids past the first 64."""
+    need_gpu()
+    specs = [LayerSpec("sliding", 256, 8, 1, 512, kv_dtype=kv_dtype), LayerSpec("full", 512, 8, 1, 0,
+                                                                                  kv_dtype=kv_dtype),
+             LayerSpec("sliding", 256, 8, 1, 512, kv_dtype=kv_dtype), LayerSpec("full", 512, 8, 1, 0,
+                                                                                  kv_dtype=kv_dtype)]
+    lens = [1, 17, 513, 4097, 30000, 700, 2]
+    sc = Scenario(specs, None, lens, seed=61 if kv_dtype == "bf16" else 62)
+    for layer in range(4):
+        sc.store(layer, [0] * len(lens), lens)
+    from workloads import normal_bf16
+    kv, maxl = i32(lens), max(lens)
+    plans = {}
+    for layer in range(4):
+        key = sc.cache.plan_key(layer)
+        if key not in plans:
+            plans[key] = sc.cache.decode_plan(layer, kv, maxl)
+    for layer in range(4):
+        q = dev_bits(normal_bf16(sc.rng, (len(lens), 8, specs[layer].head_dim)))
+        a = host_bits(sc.cache.decode(layer, kv, q, maxl))
+        b = host_bits(sc.cache.decode(layer, kv, q, maxl, plan=plans[sc.cache.plan_key(layer)]))
+        assert np.array_equal(a, b), f"layer {layer}"
+
+
+def test_planned_decode_in_graph_replays():
+    """Plans and planned decodes captured into a HIP graph: every replay equals
+    the eager result bit for bit, and the oracle within tolerance."""
+    need_gpu()
+    specs = [LayerSpec("sliding", 256, 8, 1, 64), LayerSpec("full", 512, 8, 1, 0)]
+    lens = [300, 65, 1000]
+    sc = Scenario(specs, None, lens, seed=93)
+    for layer in range(2):
+        sc.store(layer, [0] * 3, lens)
+    from workloads import normal_bf16
+    kv = i32(lens)
+    qh = [normal_bf16(sc.rng, (3, 8, specs[l].head_dim)) for l in range(2)]
+    qs = [dev_bits(q) for q in qh]
+    outs = [torch.empty_like(q) for q in qs]
+    plans = [sc.cache.decode_plan(l, kv, 1000) for l in range(2)]
+    ws, need = sc.cache.workspace(1, 3, 1000)
+
+    def step():
+        from full_attention_amd import pakv
+        for l in range(2):
+            pakv.decode_plan(sc.cache.map, l, sc.cache.pages, kv, 3, 1000, plans[l], plans[l].numel())
+            sc.cache.decode(l, kv, qs[l], 1000, out=outs[l], plan=plans[l])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for l in range(2):
+        ref = np.stack([sc.oracle.decode(l, b, qh[l][b], lens[b]) for b in range(3)])
+        assert_close(host_bits(eager[l]), ref, f"planned layer {l}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(0)
+        torch.randn(1000, device="cuda").sum()          # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs"
