@@ -85,6 +85,23 @@ __device__ __forceinline__ void dma16_s_x2(const void* base, uint32_t v0, uint32
         : "memory");
 }
 
+// One copy of such a run: copy I reads base + voff + 1024 I into LDS
+// [lds_addr + 1024 I, +1024), as a single instruction, so that copies can be
+// spread one at a time between other work.
+template <int I>
+__device__ __forceinline__ void dma16_s_at(const void* base, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3 offset:%4\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base)), "i"(1024 * I)
+        : "memory");
+}
+
 // s_waitcnt vmcnt(N), other counters untouched.
 template <int N>
 __device__ __forceinline__ void wait_vm() {

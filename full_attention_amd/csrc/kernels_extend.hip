@@ -52,10 +52,6 @@ constexpr int kTile = 32;            // kv tokens per staged tile (two pages)
 constexpr int kRankedSeqs = 256;     // sequences ordered by weight at dispatch (one per thread)
 constexpr float kRescale = 8.0f;     // raise the running max only past 2^8
 constexpr int kRuns = 4;             // copy runs per step: V(t+1) and K(t+2), one per page
-#ifndef PAKV_RUN_GAP
-#define PAKV_RUN_GAP 1
-#endif
-constexpr int kRunGapSet = PAKV_RUN_GAP;   // loop steps between copy runs (0: spread evenly)
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -174,9 +170,10 @@ struct ExtendArgs {
     float score_scale;   // sm_scale * log2(e)
 };
 
-// XOR key of a kv token's K row in LDS (16-byte granules): the 8 rows that 8
-// consecutive lanes read land in 8 different bank groups.
-__device__ __forceinline__ int k_swz(int tk) { return (tk & 3) | ((tk >> 1) & 4); }
+// XOR key of a kv token's K row in LDS (16-byte granules).  LDS serves a
+// 16-byte-per-lane read 16 lanes at a time over 64 banks; the 16 rows that 16
+// consecutive lanes read land in 16 different bank groups.
+__device__ __forceinline__ int k_swz(int tk) { return tk & 15; }
 
 template <int D>
 struct XCfg {
@@ -189,7 +186,7 @@ struct XCfg {
     static constexpr int HALF = 2 * PAGE;               // K (or V) of one 32-token tile
     static constexpr int PP = PAGE / 1024;              // 1 KiB pieces per (page, head) block
     static constexpr int NI = PP / NW;                  // pieces per wavefront per page
-    static constexpr int LDS = 4 * HALF;                // K ring of 2 tiles, V ring of 2 tiles
+    static constexpr int LDS = (4 * HALF > ROWS * D * 2) ? 4 * HALF : ROWS * D * 2;   // K, V rings; the output rows
     static constexpr int KK = D / 16;                   // 16-dim steps of the score product
     static constexpr int MT = D / 32;                   // 32-dim tiles of the output
     static_assert(KK == 2 * MT, "one score MFMA per value MFMA");
@@ -205,7 +202,7 @@ struct XCfg {
 // K piece q holds the page's rows tk = (64 q + lane) / GR (GR 16-byte
 // granules per row), granule colp ^ key(tk) of row tk landing at granule colp;
 // V piece q holds dims d = 32 q + lane / 2 of the page, half (lane & 1) ^
-// bit 2 of d.  The per-lane source offsets (less 1024 i) are the same for
+// bit 3 of d.  The per-lane source offsets (less 1024 i) are the same for
 // every page and every tile, so they are formed once.
 template <int D>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t (&k_voff)[XCfg<D>::NI], uint32_t& v_voff) {
@@ -218,7 +215,7 @@ __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t (&k_vo
         const int tk = (q * 64 + lane) / GR;
         k_voff[i] = (uint32_t)(tk * C::KROW + ((colp ^ k_swz(tk)) * 16) - 1024 * i);
     }
-    v_voff = (uint32_t)(C::NI * wave * 1024 + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 3) & 1)) * 16));
+    v_voff = (uint32_t)(C::NI * wave * 1024 + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
 }
 
 // One wavefront's run of page p of a tile (LDS slot base `slot`) from the
@@ -231,12 +228,45 @@ __device__ __forceinline__ void copy_k_run(const uint8_t* src, const uint32_t (&
     if constexpr (C::NI == 4) dma16_s_x4(src, k_voff[0], k_voff[1], k_voff[2], k_voff[3], dst);
     else dma16_s_x2(src, k_voff[0], k_voff[1], dst);
 }
+// Copy i alone of the K (or V) run of page p.
+template <int D, int I>
+__device__ __forceinline__ void copy_k_one(const uint8_t* src, const uint32_t (&k_voff)[XCfg<D>::NI], uint32_t slot,
+                                           int p, int wave) {
+    using C = XCfg<D>;
+    dma16_s_at<I>(src, k_voff[I], slot + (C::PP * p + C::NI * wave) * 1024);
+}
+template <int D, int I>
+__device__ __forceinline__ void copy_v_one(const uint8_t* src, uint32_t v_voff, uint32_t slot, int p, int wave) {
+    using C = XCfg<D>;
+    dma16_s_at<I>(src, v_voff, slot + (C::PP * p + C::NI * wave) * 1024);
+}
 template <int D>
 __device__ __forceinline__ void copy_v_run(const uint8_t* src, uint32_t v_voff, uint32_t slot, int p, int wave) {
     using C = XCfg<D>;
     const uint32_t dst = slot + (C::PP * p + C::NI * wave) * 1024;
     if constexpr (C::NI == 4) dma16_s_x4(src, v_voff, v_voff, v_voff, v_voff, dst);
     else dma16_s_x2(src, v_voff, v_voff, dst);
+}
+
+// Copy i of the run of page p: K (is_k) or V, i known once the loops unroll.
+template <int D>
+__device__ __forceinline__ void copy_piece(bool is_k, int i, const uint8_t* src, const uint32_t (&k_voff)[XCfg<D>::NI],
+                                           uint32_t v_voff, uint32_t slot, int p, int wave) {
+    if (is_k) {
+        if (i == 0) copy_k_one<D, 0>(src, k_voff, slot, p, wave);
+        else if (i == 1) copy_k_one<D, 1>(src, k_voff, slot, p, wave);
+        if constexpr (XCfg<D>::NI == 4) {
+            if (i == 2) copy_k_one<D, 2>(src, k_voff, slot, p, wave);
+            else if (i == 3) copy_k_one<D, 3>(src, k_voff, slot, p, wave);
+        }
+    } else {
+        if (i == 0) copy_v_one<D, 0>(src, v_voff, slot, p, wave);
+        else if (i == 1) copy_v_one<D, 1>(src, v_voff, slot, p, wave);
+        if constexpr (XCfg<D>::NI == 4) {
+            if (i == 2) copy_v_one<D, 2>(src, v_voff, slot, p, wave);
+            else if (i == 3) copy_v_one<D, 3>(src, v_voff, slot, p, wave);
+        }
+    }
 }
 
 // Online softmax of one score tile, in stages that the step spreads over its
@@ -305,39 +335,64 @@ __device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1) {
 }
 
 // One wavefront's step of the software pipeline: the score product of tile
-// t+1 (kb) and the value product of tile t (vb, operands pb), two independent
-// MFMA chains.  Step i of the loop issues value MFMA i and, in the first half,
-// score MFMAs 2i and 2i+1, so the scores are complete halfway through; the
-// second half runs soft(k), the stages of the softmax of tile t+1, between
-// the remaining value MFMAs, and soft_end() packs what the value MFMAs read
+// t+1 (kb) runs first, a chain of D/16 MFMAs per row block at full rate, then
+// the value product of tile t (vb, operands pb), D/16 MFMAs per row block,
+// with soft(i) between them: the stages of the softmax of tile t+1, whose
+// scores are complete by then; soft_end() packs what the value MFMAs read
 // last.  Each K or V operand read from LDS feeds the MFMAs of all NRB row
-// blocks of the wavefront.  The LDS operands are prefetched a few steps
-// ahead in rotating registers, and a scheduling barrier closes every step so
-// the compiler keeps this order (and this register footprint) instead of
-// hoisting every load.  copy(j) issues run j (of at most kRuns) of the next
-// tiles' global -> LDS copies, one run every kRunGap steps of the loop, so the
-// copies overlap the matrix work instead of stalling every wavefront at the
-// top of the step.  With HAVE_S = false only the value product runs (the
-// last tile).
+// blocks of the wavefront.  The LDS operands are prefetched a few MFMAs
+// ahead in rotating registers, and a scheduling barrier closes every loop
+// step so the compiler keeps this order (and this register footprint)
+// instead of hoisting every load.  copy(c) issues copy c (of at most
+// kRuns * NI) of the next tiles' global -> LDS copies.  The copies are spread
+// one every few loop steps over both loops: a copy holds up the wavefront
+// that issues it while the CU's address unit works through the copies ahead
+// of it, so issued together they stall the matrix work.  With HAVE_S = false
+// only the value product runs (the last tile).
 template <int D, bool HAVE_S, typename Copy, typename Soft, typename SoftEnd>
-__device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[4], int v_off,
+__device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[8], int v_off,
                                           const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
                                           const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
                                           f32x16 (&o)[16], int n_copies, Copy copy, Soft soft, SoftEnd soft_end) {
-    constexpr int KK = D / 16, MT = D / 32, H = KK / 2, PFK = 4, PFV = 4, NRB = XCfg<D>::NRB;
-    constexpr int kRunGap = kRunGapSet > 0 ? kRunGapSet : KK / kRuns;
-    static_assert((kRuns - 1) * kRunGap < KK, "every copy run needs a loop step");
-    auto ld_k = [&](int i) { return *reinterpret_cast<const u32x4*>(kb + k_off[i & 3] + (i >> 2) * 128); };
+    constexpr int KK = D / 16, MT = D / 32, PFK = 4, PFV = 4, NRB = XCfg<D>::NRB;
+    constexpr int kCopies = kRuns * XCfg<D>::NI;                  // copies per wavefront per step
+    constexpr int kCopyGap = (2 * KK) / kCopies;                   // loop steps between copies
+    static_assert(kCopyGap >= 1 && (kCopies - 1) * kCopyGap < 2 * KK, "every copy needs a loop step");
+    // loop step e of the step (score loop e = j, value loop e = KK + i)
+    auto copy_at = [&](int e) {
+        if (e % kCopyGap == 0 && e / kCopyGap < kCopies) {
+            if (e / kCopyGap < n_copies) copy(e / kCopyGap);
+        }
+    };
+    // score step i: granules 2i + h of the lane's K row, at k_off[bits 2, 1..0 of i] + 256 (i / 8)
+    auto ld_k = [&](int i) {
+        return *reinterpret_cast<const u32x4*>(kb + k_off[((i >> 2) & 1) * 4 + (i & 3)] + (i >> 3) * 256);
+    };
     // value step i: kv half st = i / MT, output tile m = i % MT
     auto ld_v = [&](int i) {
         return *reinterpret_cast<const u32x4*>(vb + (i / MT) * (16 * D * 2) + (i % MT) * 1024 + v_off);
     };
     u32x4 kr[PFK], vr[PFV];
-#pragma unroll
-    for (int p = 0; p < PFV; ++p) vr[p] = ld_v(p);
     if constexpr (HAVE_S) {
 #pragma unroll
         for (int p = 0; p < PFK; ++p) kr[p] = ld_k(p);
+#pragma unroll
+        for (int j = 0; j < KK; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                if (j == 0) s[rb] = asm_mfma_first(kr[0], qreg[rb][0]);
+                else asm_mfma_acc(s[rb], kr[j % PFK], qreg[rb][j]);
+            }
+            if (j + PFK < KK) kr[j % PFK] = ld_k(j + PFK);
+            else vr[j + PFK - KK] = ld_v(j + PFK - KK);     // the value loop's first operands
+            copy_at(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) asm_mfma_drain(s[rb]);
+    } else {
+#pragma unroll
+        for (int p = 0; p < PFV; ++p) vr[p] = ld_v(p);
     }
 #pragma unroll
     for (int i = 0; i < KK; ++i) {
@@ -347,29 +402,8 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
             else asm_mfma_agpr(o[rb * MT + i % MT], vr[i % PFV], pb[rb][i / MT]);
         }
         if (i + PFV < KK) vr[i % PFV] = ld_v(i + PFV);
-        if constexpr (HAVE_S) {
-            if (i < H) {
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * i + jj;
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) {
-                        if (j == 0) s[rb] = asm_mfma_first(kr[0], qreg[rb][0]);
-                        else asm_mfma_acc(s[rb], kr[j % PFK], qreg[rb][j]);
-                    }
-                    if (j + PFK < KK) kr[j % PFK] = ld_k(j + PFK);
-                }
-                if (i == H - 1) {
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) asm_mfma_drain(s[rb]);
-                }
-            } else {
-                soft(i - H);
-            }
-        }
-        if (i % kRunGap == 0 && i / kRunGap < kRuns) {
-            if (i / kRunGap < n_copies) copy(i / kRunGap);
-        }
+        if constexpr (HAVE_S) soft(i);
+        copy_at(KK + i);
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (HAVE_S) soft_end();
@@ -474,16 +508,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     // byte offset of a physical page's block of KV head g in either slab
     auto page_off = [&](int32_t ph) -> int64_t { return ((int64_t)ph * a.hkv + g) * C::PAGE; };
 
-    // Q^T operands: lane holds Q[row col of block rb][16 kk + 8 h .. +8]; rows
-    // past the chunk read token 0 of the chunk and are never written back
     u32x4 qreg[NRB][C::KK];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        const uint16_t* qp = a.q + ((int64_t)(q0 + my_tok[rb]) * a.hq + (int64_t)g * G + my_head[rb]) * D + 8 * h;
-#pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) qreg[rb][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
-    }
-    wait_vm<0>();
 
     const uint32_t lds0 = lds_addr_of(lds);
     auto kslot = [&](int32_t t) -> uint32_t { return lds0 + (t & 1) * C::HALF; };
@@ -493,15 +518,18 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     uint32_t k_voff[C::NI], v_voff;
     copy_offsets<D>(wave, lane, k_voff, v_voff);
 
-    // LDS offsets this lane reads: K row tau(col), granules (2 kk + h) ^ key
-    int k_off[4];
+    // LDS offsets this lane reads: K row tau(col), granules (2 kk + h) ^ key;
+    // the key has four bits, so it moves a granule within its group of 16
+    // (k_off[a * 4 + b] serves kk = 8c + 4a + b, plus 256c bytes)
+    int k_off[8];
     {
         const int j = col >> 3, hh = (col >> 2) & 1, i = col & 3;
         const int tk = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) k_off[s4] = tk * C::KROW + (((2 * s4 + h) ^ k_swz(tk)) * 16);
+        for (int s8 = 0; s8 < 8; ++s8)
+            k_off[s8] = tk * C::KROW + (((8 * (s8 >> 2) + 2 * (s8 & 3) + h) ^ k_swz(tk)) * 16);
     }
-    const int v_off = col * 32 + ((h ^ ((col >> 2) & 1)) * 16);
+    const int v_off = col * 32 + ((h ^ ((col >> 3) & 1)) * 16);
 
     // O^T tiles: row block rb, output tile m at o[rb * MT + m] (16 tiles)
     f32x16 o[16];
@@ -522,8 +550,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         return (t0 + kTile - 1 <= min(w_pmin[rb], hi - 1)) && (a.window == 0 || w_pmax[rb] - a.window + 1 <= t0);
     };
     // softmax state per row block; stage k of the softmax of tile t0 for
-    // every row block, spread (kSoftGap loop steps apart) over the second
-    // half of a step
+    // every row block, spread (kSoftGap loop steps apart) over the value
+    // product of a step
     f32x16 s[NRB];
     u32x4 pb[NRB][2];
     SoftRow sr[NRB];
@@ -539,8 +567,10 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) softmax_pack_hi(s[rb], pb[rb][1]);
     };
-    constexpr int kSoftGap = (C::KK / 2) / 8 > 0 ? (C::KK / 2) / 8 : 1;
-    static_assert(kSoftGap * (kSoftStages - 1) < C::KK / 2, "softmax stages must fit the second half of a step");
+    constexpr int kSoftGap = C::KK / 8;
+    // the stages fit the value loop, and stage 6 (which overwrites pb[rb][0])
+    // comes after the value MFMAs that read it (steps 0 .. MT - 1)
+    static_assert(kSoftGap * (kSoftStages - 1) < C::KK && kSoftGap * 6 >= C::MT, "softmax stage placement");
     // O of row block rb times the factor its softmax left, once the value
     // MFMAs that wrote O have landed; before the next value product
     auto apply_rescale = [&]() __attribute__((always_inline)) {
@@ -561,7 +591,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         uint8_t* vbuf = lds + 2 * C::HALF + (t & 1) * C::HALF;
         for (int idx = tid; idx < 4 * D; idx += C::THREADS) {
             const int p = idx / (2 * D), d = (idx >> 1) % D, hp = idx & 1;
-            const int half = hp ^ ((d >> 2) & 1);
+            const int half = hp ^ ((d >> 3) & 1);
             const int32_t tb = t0 + 16 * p + 8 * half;
             u32x4* gp = reinterpret_cast<u32x4*>(vbuf + p * C::PAGE + d * 32 + hp * 16);
             u32x4 v = *gp;
@@ -594,6 +624,17 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
             copy_k_run<D>(k_src + ok0, k_voff, kslot(1), 0, wave);
             copy_k_run<D>(k_src + ok1, k_voff, kslot(1), 1, wave);
         }
+    }
+    // Q^T operands, loaded while the first tiles are in flight: lane holds
+    // Q[row col of block rb][16 kk + 8 h .. +8]; rows past the chunk read token
+    // 0 of the chunk and are never written back
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const uint16_t* qp = a.q + ((int64_t)(q0 + my_tok[rb]) * a.hq + (int64_t)g * G + my_head[rb]) * D + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) qreg[rb][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
+    }
+    if (n_tiles > 0) {
         wait_vm<0>();
         lds_barrier();
         if (wave_live) {
@@ -603,7 +644,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
                 s[rb] = asm_mfma_first(*reinterpret_cast<const u32x4*>(kbuf + k_off[0]), qreg[rb][0]);
 #pragma unroll
                 for (int kk = 1; kk < C::KK; ++kk)
-                    asm_mfma_acc(s[rb], *reinterpret_cast<const u32x4*>(kbuf + k_off[kk & 3] + (kk >> 2) * 128),
+                    asm_mfma_acc(s[rb], *reinterpret_cast<const u32x4*>(kbuf + k_off[((kk >> 2) & 1) * 4 + (kk & 3)] +
+                                                                        (kk >> 3) * 256),
                                  qreg[rb][kk]);
                 asm_mfma_drain(s[rb]);
             }
@@ -630,14 +672,16 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
             ok1 = page_off(page_id(2 * t + 5));
         }
         const uint32_t vs = vslot(t + 1), ks = kslot(t + 2);
-        // run j of this step's copies: V(t+1) pages 0, 1, then K(t+2) pages 0, 1
-        auto copy = [&](int j) {
-            if (j == 0) copy_v_run<D>(v_src + ov0, v_voff, vs, 0, wave);
-            else if (j == 1) copy_v_run<D>(v_src + ov1, v_voff, vs, 1, wave);
-            else if (j == 2) copy_k_run<D>(k_src + ok0, k_voff, ks, 0, wave);
-            else copy_k_run<D>(k_src + ok1, k_voff, ks, 1, wave);
+        // copy c of this step: run c / NI (V(t+1) pages 0, 1, then K(t+2) pages 0,
+        // 1), copy c % NI of it
+        auto copy = [&](int c) {
+            const int j = c / C::NI, i = c % C::NI;
+            if (j == 0) copy_piece<D>(false, i, v_src + ov0, k_voff, v_voff, vs, 0, wave);
+            else if (j == 1) copy_piece<D>(false, i, v_src + ov1, k_voff, v_voff, vs, 1, wave);
+            else if (j == 2) copy_piece<D>(true, i, k_src + ok0, k_voff, v_voff, ks, 0, wave);
+            else copy_piece<D>(true, i, k_src + ok1, k_voff, v_voff, ks, 1, wave);
         };
-        const int n_copies = k_next ? 4 : 2;
+        const int n_copies = (k_next ? 4 : 2) * C::NI;
         zero_v_edges(t);
         if (wave_live) {
             const uint8_t* kbuf = lds + ((t + 1) & 1) * C::HALF;
@@ -669,23 +713,40 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         settle_tiles(o);   // the last value MFMAs have landed before the output reads them
     }
 
-    wait_vm<0>();   // no copy may still be landing in LDS when the workgroup ends
+    // ---- output: O / l as bf16, through LDS so that every store is a whole row
+    // (or two) of 16-byte lanes.  Row r of the workgroup sits at r * 2D bytes,
+    // its 16-byte granule q at granule q ^ (r mod D/8) (the 32 rows a
+    // wavefront writes at once land in different banks).
+    wait_vm<0>();   // no copy is still landing in LDS
+    lds_barrier();  // ... and every wavefront is done with the rings
+    constexpr int RB = 2 * D, GM = D / 8 - 1;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         const float l_tot = sum_halves(l_run[rb]);
-        if (!row_ok[rb]) continue;
-        const float inv = 1.0f / l_tot;
-        uint16_t* op = a.out + ((int64_t)(q0 + my_tok[rb]) * a.hq + (int64_t)g * G + my_head[rb]) * D;
+        if (!wave_live) continue;
+        const float inv = row_ok[rb] ? 1.0f / l_tot : 0.0f;
+        const int r = wave * 32 * NRB + 32 * rb + col;
+        uint8_t* rowp = lds + r * RB;
 #pragma unroll
         for (int m = 0; m < C::MT; ++m) {
             const f32x16& om = o[rb * C::MT + m];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 32 * m + 8 * j + 4 * h;
-                *reinterpret_cast<u32x2*>(op + d) = u32x2{cvt_pk_bf16(om[4 * j] * inv, om[4 * j + 1] * inv),
-                                                          cvt_pk_bf16(om[4 * j + 2] * inv, om[4 * j + 3] * inv)};
+                const int q = 4 * m + j;         // granule of dims 32m + 8j .. +8
+                *reinterpret_cast<u32x2*>(rowp + ((q ^ (r & GM)) << 4) + 8 * h) =
+                    u32x2{cvt_pk_bf16(om[4 * j] * inv, om[4 * j + 1] * inv),
+                          cvt_pk_bf16(om[4 * j + 2] * inv, om[4 * j + 3] * inv)};
             }
         }
+    }
+    lds_barrier();
+    const int32_t n_rows = min(C::ROWS, rows - row0);
+    for (int idx = tid; idx < n_rows * (D / 8); idx += C::THREADS) {
+        const int r = idx / (D / 8), q = idx % (D / 8);
+        const int32_t row = row0 + r;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RB + ((q ^ (r & GM)) << 4));
+        uint16_t* op = a.out + ((int64_t)(q0 + row / G) * a.hq + (int64_t)g * G + row % G) * D + 8 * q;
+        *reinterpret_cast<u32x4*>(op) = v;
     }
 }
 
