@@ -277,19 +277,28 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
     const uint8_t* kp = a.k_slab + blk;
     const uint8_t* vp = a.v_slab + blk;
     const uint32_t kb = lds_addr_of(buf), vb = kb + C::PAGE;
-    // K: LDS granule G holds row G / (ROW/16), column (G % (ROW/16)) ^ (row & 7)
+    // K: LDS granule G holds row G / (ROW/16), column (G % (ROW/16)) ^ (row & 15)
+    // (LDS serves 16-byte reads 16 lanes at a time over 64 banks: the 16 rows
+    // read at once land in 16 different bank groups)
 #pragma unroll
     for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
         const int inst = wave + kWaves * i;
         const int G = inst * 64 + lane;
         const int row = G / (C::ROW / 16), colp = G % (C::ROW / 16);
-        dma16(kp + row * C::ROW + (colp ^ (row & 7)) * 16, kb + inst * 1024);
+        dma16(kp + row * C::ROW + (colp ^ (row & 15)) * 16, kb + inst * 1024);
     }
-    // V: the dim-major page block, copied as is
+    // V: the dim-major page block; for bf16 the two 16-byte halves of dim d
+    // trade places when bit 3 of d is set, so that the 16 dims read at once
+    // land in different bank groups
 #pragma unroll
     for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
         const int inst = wave + kWaves * i;
-        dma16(vp + inst * 1024 + lane * 16, vb + inst * 1024);
+        if constexpr (!INT8) {
+            const int gp = inst * 64 + lane, d = gp >> 1;
+            dma16(vp + d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16), vb + inst * 1024);
+        } else {
+            dma16(vp + inst * 1024 + lane * 16, vb + inst * 1024);
+        }
     }
     if constexpr (INT8) {
         // wave w copies 32 bytes of the page's 128 bytes of scales (k then v)
@@ -527,9 +536,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                 const int e0 = dq + 32 * kk + 8 * qg;          // first of 8 dims
                 u32x4 ka;
                 if constexpr (!INT8) {
-                    ka = *reinterpret_cast<const u32x4*>(krow + (((e0 >> 3) ^ (row & 7)) * 16));
+                    ka = *reinterpret_cast<const u32x4*>(krow + (((e0 >> 3) ^ (row & 15)) * 16));
                 } else {
-                    const u32x2 w = *reinterpret_cast<const u32x2*>(krow + (((e0 >> 4) ^ (row & 7)) * 16) + (e0 & 8));
+                    const u32x2 w = *reinterpret_cast<const u32x2*>(krow + (((e0 >> 4) ^ (row & 15)) * 16) + (e0 & 8));
                     ka = u32x4{i8x2_to_bf16x2(w.x, 0), i8x2_to_bf16x2(w.x, 2),
                                i8x2_to_bf16x2(w.y, 0), i8x2_to_bf16x2(w.y, 2)};
                 }
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             const int d = dq + 16 * m + col;
             u32x2 va;
             if constexpr (!INT8) {
-                va = *reinterpret_cast<const u32x2*>(vbuf + d * 32 + 8 * qg);
+                va = *reinterpret_cast<const u32x2*>(vbuf + d * 32 + ((((qg >> 1) ^ (d >> 3)) & 1) << 4) + 8 * (qg & 1));
                 if (!full) {
                     va.x &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
                     va.y &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
