@@ -30,6 +30,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// The same rounding (to nearest even) in one instruction, v_cvt_pk_bf16_f32;
+// a NaN comes out as a quiet NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
+}
+
 // 16x16x32 bf16 MFMA: C[16x16] += A[16x32] * B[32x16].  Lane l supplies row
 // (l % 16) of A and column (l % 16) of B, each with the 8 contraction indices
 // of group l / 16; it receives C rows 4*(l/16) .. +3 of column l % 16.
@@ -44,17 +51,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Lanes l, l^16, l^32, l^48 hold the same column.  v_permlane16_swap trades
+// odd 16-lane rows of its first operand with even rows of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; given the same register twice, the two results hold, in every lane,
+// the lane's own value and its partner's (16, then 32 lanes away), without
+// the round trip through LDS that a shuffle takes.
 __device__ __forceinline__ float wave_max_across_groups(float v) {
-    // lanes l, l^16, l^32, l^48 hold the same column
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The sum of the four lanes, added in the same order in every lane (row 0 + row 1, row 2 + row 3,
+// then the two), so all four hold the same bits.
 __device__ __forceinline__ float wave_sum_across_groups(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi) {

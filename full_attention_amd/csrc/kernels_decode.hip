@@ -258,15 +258,29 @@ __device__ __forceinline__ uint32_t sched_ids(const DecodeArgs& a, int32_t c0, i
 }
 
 // Q^T operand of a wave's dim quarter: column `col` = head g*G + col (zero
-// for padding columns), dims dq + 32*kk + 8*qg .. +8.
+// for padding columns), dims dq + 32*kk + 8*qg .. +8.  The loads are inline
+// assembly, so the compiler does not track them: a tracked load of Q that is
+// still pending where the loop begins makes it wait on the vector-memory
+// counter before every use of Q inside the loop, which (that counter being
+// in order) drains every copy in flight on every chunk.  They are issued
+// before a chunk's copies and complete before them; take_q() then hands the
+// registers to the compiler, after the wait that covers them.
 template <int D>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, const Unit& x, int32_t G, int col, int qg, int dq,
                                        u32x4 (&qreg)[D / 128]) {
-    const bool real = col < G;
-    const uint16_t* qp = a.q + ((int64_t)x.b * a.hq + (int64_t)x.g * G + (real ? col : 0)) * D + dq + 8 * qg;
+    const uint16_t* qp = a.q + ((int64_t)x.b * a.hq + (int64_t)x.g * G + (col < G ? col : 0)) * D + dq + 8 * qg;
 #pragma unroll
     for (int kk = 0; kk < D / 128; ++kk)
-        qreg[kk] = real ? *reinterpret_cast<const u32x4*>(qp + 32 * kk) : u32x4{0, 0, 0, 0};
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qreg[kk]) : "v"(qp + 32 * kk) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void take_q(u32x4 (&qreg)[N], bool real) {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) {
+        asm volatile("" : "+v"(qreg[kk]));
+        if (!real) qreg[kk] = u32x4{0, 0, 0, 0};
+    }
 }
 
 template <int D, bool INT8>
@@ -421,8 +435,8 @@ __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32
             if (!on[i]) continue;
             const float inv = 1.0f / L[i];
             uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl[i]) * D + d0[i];
-            *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv),
-                                                  pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv)};
+            *reinterpret_cast<u32x2*>(op) = u32x2{cvt_pk_bf16(acc[i][0] * inv, acc[i][1] * inv),
+                                                  cvt_pk_bf16(acc[i][2] * inv, acc[i][3] * inv)};
         }
     }
 }
@@ -477,6 +491,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     int32_t kc = min(kc_first, uc.n - 1);
     Unit ui = uc;                                 // issue cursor
     int32_t ki = kc;
+    const int dq = wave * (D / 4);
+    u32x4 qreg[C::KK];
+    load_q<D>(a, uc, G, col, qg, dq, qreg);       // complete once chunk 0's copies are
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
@@ -484,9 +501,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             advance(a, st, U, ui, ki);
         }
     }
-    const int dq = wave * (D / 4);
-    u32x4 qreg[C::KK];
-    load_q<D>(a, uc, G, col, qg, dq, qreg);
 
     f32x4 o[C::MT];
 #pragma unroll
@@ -497,14 +511,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
         lds_barrier();
         if (kc == 0 || i == 0) {
-            // a new unit inside the run: its Q.  The wait drains the copies in
-            // flight, but only here: with no load left pending across the
-            // loop's back edge, the compiler has no reason to wait on the
-            // (in-order) vector-memory counter anywhere else in the loop.
+            // a new unit: its Q.  The first was issued before chunk 0's copies,
+            // so the wait above covered it; a later one drains the copies in
+            // flight, but only here, once per unit.
             if (i > 0) {
                 load_q<D>(a, uc, G, col, qg, dq, qreg);
                 wait_vm<0>();
             }
+            take_q(qreg, col < G);
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
             m_run = -INFINITY;
@@ -576,11 +590,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         mx = wave_max_across_groups(mx);
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        // v_exp_f32 directly: a weight below 2^-126 of the row's largest
+        // becomes zero instead of a denormal
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         float p[4], psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            p[e] = exp2f(sc[e] - m_use);
+            p[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
             psum += p[e];
         }
         l_run = l_run * alpha + psum;
@@ -592,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             if constexpr (INT8) x *= vs[e];
             pv[e] = valid[e] ? x : 0.0f;
         }
-        const u32x2 pb = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        const u32x2 pb = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
         const bool full = (t0 >= uc.lo) && (t0 + kChunk <= uc.hi);
 
         // ---- values: this wave's quarter of the output dims ------------------
@@ -626,7 +642,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int m = 0; m < C::MT; ++m)
                         *reinterpret_cast<u32x2*>(op + 16 * m + 4 * qg) =
-                            u32x2{pack_bf16x2(o[m][0] * inv, o[m][1] * inv), pack_bf16x2(o[m][2] * inv, o[m][3] * inv)};
+                            u32x2{cvt_pk_bf16(o[m][0] * inv, o[m][1] * inv), cvt_pk_bf16(o[m][2] * inv, o[m][3] * inv)};
                 }
             } else {
                 const int64_t slot = ((int64_t)blockIdx.x + uc.u) * G;
