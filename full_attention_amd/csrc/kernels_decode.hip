@@ -288,7 +288,7 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
                                             int wave, int lane) {
     using C = Cfg<D, INT8>;
     const int64_t blk = ((int64_t)phys * a.hkv + x.g) * C::PAGE;
-    const uint8_t* kp = a.k_slab + blk;
+    const uint8_t* kp = a.k_slab + blk;       // wave-uniform bases; per-lane 32-bit offsets
     const uint8_t* vp = a.v_slab + blk;
     const uint32_t kb = lds_addr_of(buf), vb = kb + C::PAGE;
     // K: LDS granule G holds row G / (ROW/16), column (G % (ROW/16)) ^ (row & 15)
@@ -299,7 +299,7 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
         const int inst = wave + kWaves * i;
         const int G = inst * 64 + lane;
         const int row = G / (C::ROW / 16), colp = G % (C::ROW / 16);
-        dma16(kp + row * C::ROW + (colp ^ (row & 15)) * 16, kb + inst * 1024);
+        dma16_s(kp, (uint32_t)(row * C::ROW + (colp ^ (row & 15)) * 16), kb + inst * 1024);
     }
     // V: the dim-major page block; for bf16 the two 16-byte halves of dim d
     // trade places when bit 3 of d is set, so that the 16 dims read at once
@@ -309,9 +309,9 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
         const int inst = wave + kWaves * i;
         if constexpr (!INT8) {
             const int gp = inst * 64 + lane, d = gp >> 1;
-            dma16(vp + d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16), vb + inst * 1024);
+            dma16_s(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
         } else {
-            dma16(vp + inst * 1024 + lane * 16, vb + inst * 1024);
+            dma16_s(vp, (uint32_t)(inst * 1024 + lane * 16), vb + inst * 1024);
         }
     }
     if constexpr (INT8) {
@@ -355,6 +355,19 @@ __device__ __forceinline__ f32x2 get2(const float* p) {
     asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
     return v;
 }
+// Scalar base + 32-bit byte offset forms: one address VGPR per partial
+// serves all of a thread's items through the immediate offset.
+template <int OFF>
+__device__ __forceinline__ f32x4 get4s(const float* base, uint32_t voff) {
+    f32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 sc1" : "=v"(v) : "v"(voff), "s"(base), "i"(OFF) : "memory");
+    return v;
+}
+__device__ __forceinline__ f32x2 get2s(const float* base, uint32_t voff) {
+    f32x2 v;
+    asm volatile("global_load_dwordx2 %0, %1, %2 sc1" : "=v"(v) : "v"(voff), "s"(base) : "memory");
+    return v;
+}
 template <int N, typename T>
 __device__ __forceinline__ void await(T (&regs)[N]) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -374,70 +387,73 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 }
 
 // Merges the partials of unit x (slots w + x.u for w in [w0, w1], in that
-// order) and writes the G heads' bf16 outputs.  A thread owns up to two
-// (head, 4-dim) items per pass and reads 8 slots per batch, so a unit of up
-// to 8 partials with G * D <= 2048 is merged in one round trip.
+// order) and writes the G heads' bf16 outputs.  Thread t owns IPT = D/128
+// 4-dim items of one head, dims 4 (t % 32) + 128 j, so one (m, l) pair per
+// partial serves all of them while each load instruction still reads 512
+// contiguous bytes per head; a pass covers 8 heads.  Each batch issues all its loads before
+// the first wait: a unit of up to BATCH partials is merged in one round trip
+// (the merging workgroup's own bandwidth bounds it, so fewer, fuller round
+// trips are what shorten it).
 template <int D>
 __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
-    constexpr int BATCH = 8;
-    const int n_items = G * (D / 4);
-    for (int base = 0; base < n_items; base += 512) {
-        int hl[2], d0[2];
-        bool on[2];
+    constexpr int IPT = D / 128;
+    constexpr int TPH = (D / 4) / IPT;                 // threads per head (32)
+    constexpr int BATCH = (D == 512) ? 7 : 12;
+    static_assert(IPT == 2 || IPT == 4, "items per thread");
+    const int d0 = (t % TPH) * 4;
+    // byte offsets below are 32-bit: the partial buffers are sized by the
+    // host to (grid + units) * G * (D + 2) floats, far below 4 GiB
+    const float* o_base = reinterpret_cast<const float*>(uniform_ptr(a.part_o));
+    const float* ml_base = reinterpret_cast<const float*>(uniform_ptr(a.part_ml));
+    for (int hb = 0; hb < G; hb += 256 / TPH) {
+        const int hl = hb + t / TPH;
+        if (hl >= G) continue;
+        float M = -INFINITY, L = 0.f;
+        f32x4 acc[IPT];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int it = base + i * 256 + t;
-            on[i] = it < n_items;
-            hl[i] = on[i] ? it / (D / 4) : 0;
-            d0[i] = on[i] ? (it % (D / 4)) * 4 : 0;
-        }
-        float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int j = 0; j < IPT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int32_t wb = w0; wb <= w1; wb += BATCH) {
-            f32x2 ml[2 * BATCH];
-            f32x4 ov[2 * BATCH];
+            f32x2 ml[BATCH];
+            f32x4 ov[BATCH * IPT];
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
-                const int32_t w = min(wb + k, w1);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    if (on[i]) {
-                        const int64_t sl = ((int64_t)w + x.u) * G + hl[i];
-                        ml[i * BATCH + k] = get2(a.part_ml + sl * 2);
-                        ov[i * BATCH + k] = get4(a.part_o + sl * D + d0[i]);
-                    }
+                const uint32_t sl = (uint32_t)((min(wb + k, w1) + x.u) * G + hl);
+                ml[k] = get2s(ml_base, sl * 8u);
+                const uint32_t ob = (sl * D + d0) * 4u;
+                ov[k * IPT + 0] = get4s<0>(o_base, ob);
+                ov[k * IPT + 1] = get4s<512>(o_base, ob);
+                if constexpr (IPT > 2) {
+                    ov[k * IPT + 2] = get4s<1024>(o_base, ob);
+                    ov[k * IPT + 3] = get4s<1536>(o_base, ob);
                 }
             }
             await(ml);
             await(ov);
+            float Mb = M;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float Mb = M[i];
+            for (int k = 0; k < BATCH; ++k)
+                if (wb + k <= w1) Mb = fmaxf(Mb, ml[k].x);
+            const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
+            const float r = exp2f(M - Mb_use);            // rescale what came before
+            L *= r;
 #pragma unroll
-                for (int k = 0; k < BATCH; ++k)
-                    if (wb + k <= w1) Mb = fmaxf(Mb, ml[i * BATCH + k].x);
-                const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
-                const float r = exp2f(M[i] - Mb_use);        // rescale what came before
-                L[i] *= r;
-                acc[i] *= r;
+            for (int j = 0; j < IPT; ++j) acc[j] *= r;
 #pragma unroll
-                for (int k = 0; k < BATCH; ++k) {
-                    if (wb + k > w1) break;
-                    const float wt = exp2f(ml[i * BATCH + k].x - Mb_use);
-                    L[i] += wt * ml[i * BATCH + k].y;
-                    acc[i] += wt * ov[i * BATCH + k];
-                }
-                M[i] = Mb;
+            for (int k = 0; k < BATCH; ++k) {
+                // slots past w1 repeat w1's (finite) partial with weight zero
+                const float wt = (wb + k <= w1) ? exp2f(ml[k].x - Mb_use) : 0.0f;
+                L += wt * ml[k].y;
+#pragma unroll
+                for (int j = 0; j < IPT; ++j) acc[j] += wt * ov[k * IPT + j];
             }
+            M = Mb;
         }
+        const float inv = 1.0f / L;
+        uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl) * D + d0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (!on[i]) continue;
-            const float inv = 1.0f / L[i];
-            uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl[i]) * D + d0[i];
-            *reinterpret_cast<u32x2*>(op) = u32x2{cvt_pk_bf16(acc[i][0] * inv, acc[i][1] * inv),
-                                                  cvt_pk_bf16(acc[i][2] * inv, acc[i][3] * inv)};
-        }
+        for (int j = 0; j < IPT; ++j)
+            *reinterpret_cast<u32x2*>(op + 128 * j) = u32x2{cvt_pk_bf16(acc[j][0] * inv, acc[j][1] * inv),
+                                                          cvt_pk_bf16(acc[j][2] * inv, acc[j][3] * inv)};
     }
 }
 
@@ -512,17 +528,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         lds_barrier();
         if (kc == 0 || i == 0) {
             // a new unit: its Q.  The first was issued before chunk 0's copies,
-            // so the wait above covered it; a later one drains the copies in
-            // flight, but only here, once per unit.
-            if (i > 0) {
-                load_q<D>(a, uc, G, col, qg, dq, qreg);
-                wait_vm<0>();
-            }
+            // so the wait above covered it; a later one was issued when the
+            // previous unit ended, after the copies in flight, and this wait
+            // drains them too, but only here, once per unit.
+            if (i > 0) wait_vm<0>();
             take_q(qreg, col < G);
-#pragma unroll
-            for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m_run = -INFINITY;
-            l_run = 0.0f;
         }
         {
             const int32_t j = i + C::NBUF - 1;        // chunk to copy now
@@ -661,7 +671,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                 }
             }
         }
+        // a unit ends: the next one's Q, and its accumulators start empty (set
+        // here rather than at its first chunk, so that neither o nor Q is live
+        // across the merge above)
+        const bool ended = (kc == uc.n - 1);
         advance(a, st, U, uc, kc);
+        if (ended && i + 1 < total) {
+            load_q<D>(a, uc, G, col, qg, dq, qreg);
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run = -INFINITY;
+            l_run = 0.0f;
+        }
     }
     wait_vm<0>();
 }
