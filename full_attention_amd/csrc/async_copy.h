@@ -49,6 +49,22 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
         : "memory");
 }
 
+// The same copy marked non-temporal (nt): for bytes read once per call, such
+// as a decode's K/V pages, so that streaming them does not push out of the
+// caches the small data that every workgroup reads (schedule, Q, partials).
+__device__ __forceinline__ void dma16_s_nt(const void* base, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
+        : "memory");
+}
+
 // Runs of copies from one wave-uniform base with M0 written once: copy i
 // reads base + voff_i + 1024 i into LDS [lds_addr + 1024 i, +1024) (the
 // instruction's immediate offset is added to both the global and the LDS

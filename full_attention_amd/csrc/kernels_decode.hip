@@ -299,7 +299,7 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
         const int inst = wave + kWaves * i;
         const int G = inst * 64 + lane;
         const int row = G / (C::ROW / 16), colp = G % (C::ROW / 16);
-        dma16_s(kp, (uint32_t)(row * C::ROW + (colp ^ (row & 15)) * 16), kb + inst * 1024);
+        dma16_s_nt(kp, (uint32_t)(row * C::ROW + (colp ^ (row & 15)) * 16), kb + inst * 1024);
     }
     // V: the dim-major page block; for bf16 the two 16-byte halves of dim d
     // trade places when bit 3 of d is set, so that the 16 dims read at once
@@ -309,9 +309,9 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
         const int inst = wave + kWaves * i;
         if constexpr (!INT8) {
             const int gp = inst * 64 + lane, d = gp >> 1;
-            dma16_s(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
+            dma16_s_nt(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
         } else {
-            dma16_s(vp, (uint32_t)(inst * 1024 + lane * 16), vb + inst * 1024);
+            dma16_s_nt(vp, (uint32_t)(inst * 1024 + lane * 16), vb + inst * 1024);
         }
     }
     if constexpr (INT8) {
