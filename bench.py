@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of a graph")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="owners store the new K/V in a launch of their own before decoding")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     return ap.parse_args()
@@ -174,19 +176,25 @@ def setup_decode(torch):
     return st
 
 
-def decode_step(st):
+def decode_step(st, fused=True):
     """Store the new token's K/V on the owners and decode every layer.  The
     split of the keys is planned once per step for each kind of layer (window,
-    Hkv) and shared by all layers of that kind."""
+    Hkv) and shared by all layers of that kind.  An owner with bf16 K/V stores
+    and decodes in one launch (decode_append); fused=False makes the store its
+    own launch, as an int8 owner always does."""
     from full_attention_amd import pakv as pakv_mod
     cache = st["cache"]
     for key, (layer, buf) in st["plans"].items():
         pakv_mod.decode_plan(cache.map, layer, cache.pages, st["kv_len_t"], st["B"], st["max_kv_len"],
                              buf, buf.numel())
-    for l in range(len(st["layers"])):
-        if l in st["new_k"]:
-            cache.store(l, st["cu_new"], st["pos_new"], st["new_k"][l], st["new_v"][l])
+    for l, s in enumerate(st["layers"]):
         plan = st["plans"][cache.plan_key(l)][1]
+        if l in st["new_k"] and (s.kv_dtype != "bf16" or not fused):
+            cache.store(l, st["cu_new"], st["pos_new"], st["new_k"][l], st["new_v"][l])
+        elif l in st["new_k"]:
+            cache.decode_append(l, plan, st["new_k"][l], st["new_v"][l], st["q"][l], st["max_kv_len"],
+                                out=st["out"][l])
+            continue
         cache.decode(l, st["kv_len_t"], st["q"][l], st["max_kv_len"], out=st["out"][l], plan=plan)
 
 
@@ -385,14 +393,15 @@ def main():
         del src, dst
     st = setup_decode(torch)
     nl = len(st["layers"])
-    ms_step, graph = run_graph_or_eager(torch, lambda: decode_step(st), args.steps, args.warmup, args.eager)
+    fused = not args.separate_store
+    ms_step, graph = run_graph_or_eager(torch, lambda: decode_step(st, fused), args.steps, args.warmup, args.eager)
     per_layer = decode_bytes(st)
     step_bytes = sum(kv + qo for kv, qo in per_layer)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
     # per-kernel durations of the decode partial pass (one launch per layer)
     ksteps = max(1, min(args.steps, 10))
-    mean_ms, method = kernel_durations(torch, pakv, lambda: decode_step(st), nl, pakv.TIME_DECODE, ksteps)
+    mean_ms, method = kernel_durations(torch, pakv, lambda: decode_step(st, fused), nl, pakv.TIME_DECODE, ksteps)
     groups = {}
     for l, s in enumerate(st["layers"]):
         key = f"decode_kernel<{s.head_dim},{'int8' if s.kv_dtype == 'int8' else 'bf16'}>"
@@ -418,7 +427,9 @@ def main():
             "config": {"workload": wl_name + " (28 sliding D256 W512 + 7 full D512; Hq 8, Hkv 1; "
                                    "layers 15-34 KV-shared, 15 slabs; context U[512,4096]; page 16)",
                        "global_batch": st["B"], "seq_len": int(st["max_kv_len"]),
-                       "layers": nl, "step": "plan 2 kinds of layer + store new K/V on 15 owners + decode 35 layers",
+                       "layers": nl, "step": ("plan 2 kinds of layer + 15 owners store their new K/V and decode in one launch each"
+                                         " + 20 shared layers decode") if fused else
+                                        "plan 2 kinds of layer + store new K/V on 15 owners + decode 35 layers",
                        "launch": "eager" if args.eager else "HIP graph replay",
                        "algorithmic_bytes_per_step": int(step_bytes)},
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

@@ -110,6 +110,18 @@ class PagedKVCache:
                                            max_kv_len, ws, ws.numel(), stream)
         return out
 
+    def decode_append(self, layer, plan, k_new, v_new, q, max_kv_len, out=None, stream=None):
+        """Stores this step's K/V row of every sequence (at kv_len - 1, where
+        kv_len is what `plan` was made from) and decodes, in one launch; the
+        same as store() then decode(plan=plan).  A shared layer only decodes."""
+        nseq = q.shape[0]
+        if out is None:
+            out = torch.empty_like(q)
+        ws, need = self.workspace(layer, nseq, max_kv_len)
+        pakv.paged_attn_decode_append(self.map, layer, self.pages, plan, plan.numel(), k_new, v_new, q, out, nseq,
+                                      max_kv_len, ws, ws.numel(), stream)
+        return out
+
     def extend(self, layer, cu_q, prefix_lens, q, max_q_len, max_kv_len, out=None, stream=None):
         nseq = cu_q.shape[0] - 1
         if out is None:

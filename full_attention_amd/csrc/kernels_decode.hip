@@ -72,6 +72,11 @@ struct DecodeArgs {
     uint32_t* arrivals;     // [U] partials written per unit; zero between calls
     float* part_o;          // [grid + U][G][D]
     float* part_ml;         // [grid + U][G][2]
+    // append (bf16 slabs only): this step's K/V row of each (sequence, KV
+    // head), [B][Hkv][D], stored at position L - 1 and attended as that key
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int32_t append;
 };
 
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
@@ -96,7 +101,10 @@ struct Cfg {
     static constexpr int PER = KV_DMA + (INT8 ? 1 : 0);
     static constexpr int SX = kWaves * 64 * 16;             // partial-score exchange
     static constexpr int SEQ = (2 * (pakv::kDecodeMaxSeqs + 1) * 4 + 15) & ~15;   // per-sequence table
-    static constexpr int LDS = NBUF * BUF + SX + SEQ;
+    // append: per ring slot, the new V row (D bf16) and the page id it goes to
+    static constexpr int STAGE = INT8 ? 0 : D * 2;
+    static constexpr int NEWP = INT8 ? 0 : 16;
+    static constexpr int LDS = NBUF * BUF + SX + SEQ + NBUF * STAGE + NEWP;
     static constexpr int KK = D / 128;                      // 32-dim steps in a wave's quarter
     static constexpr int MT = D / 64;                       // 16-dim output tiles in a quarter
     static_assert(LDS <= 80 * 1024, "two workgroups per CU");
@@ -283,14 +291,52 @@ __device__ __forceinline__ void take_q(u32x4 (&qreg)[N], bool real) {
     }
 }
 
+// Copies of a chunk into a ring slot.  In an append call, a unit's last
+// chunk holds the new key at position L - 1, whose row in the slab is not
+// written yet: the page's copy skips K row r = (L - 1) % 16, which the wave
+// that owns it copies from k_new instead (same swizzle, so no two copies
+// write the same LDS bytes), and wave 0 first stages the new V row (the V page
+// is dim-major: the new token is two bytes in every 32) for the consumer to
+// patch in.  Every wave still issues at least PER copies for the chunk, and
+// the staging copy comes before them, so the per-chunk waits still cover
+// everything (they can only wait for one copy more than needed).
 template <int D, bool INT8>
 __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, uint8_t* buf, const Unit& x,
-                                            int wave, int lane) {
+                                            bool last, uint8_t* stage, int32_t* newp, int wave, int lane) {
     using C = Cfg<D, INT8>;
     const int64_t blk = ((int64_t)phys * a.hkv + x.g) * C::PAGE;
     const uint8_t* kp = a.k_slab + blk;       // wave-uniform bases; per-lane 32-bit offsets
     const uint8_t* vp = a.v_slab + blk;
     const uint32_t kb = lds_addr_of(buf), vb = kb + C::PAGE;
+    if constexpr (!INT8) {
+        if (a.append && last) {
+            const int64_t nrow = ((int64_t)x.b * a.hkv + x.g) * D;     // the (b, g) row of k_new / v_new
+            const int r = (x.hi - 1) & 15;                              // slot of position L - 1
+            if (wave == 0) {
+                if (lane < D / 8) dma16_s(a.v_new + nrow, (uint32_t)(lane * 16), lds_addr_of(stage));
+                if (lane == 0) *newp = phys;
+            }
+#pragma unroll
+            for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
+                const int inst = wave + kWaves * i;
+                const int G = inst * 64 + lane;
+                const int row = G / (C::ROW / 16), colp = G % (C::ROW / 16);
+                if (row != r) dma16_s_nt(kp, (uint32_t)(row * C::ROW + (colp ^ (row & 15)) * 16), kb + inst * 1024);
+            }
+            // row r: ROW/16 granules, granule c landing at (c ^ (r & 15)); its
+            // copy instruction(s) belong to wave (r / rows per 1 KiB) % 4
+            constexpr int RPI = 1024 / C::ROW;                          // K rows per 1 KiB copy (1 or 2)
+            if (wave == (r / RPI) % kWaves && lane < C::ROW / 16)
+                dma16_s(a.k_new + nrow, (uint32_t)((lane ^ (r & 15)) * 16), kb + r * C::ROW);
+#pragma unroll
+            for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
+                const int inst = wave + kWaves * i;
+                const int gp = inst * 64 + lane, d = gp >> 1;
+                dma16_s_nt(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
+            }
+            return;
+        }
+    }
     // K: LDS granule G holds row G / (ROW/16), column (G % (ROW/16)) ^ (row & 15)
     // (LDS serves 16-byte reads 16 lanes at a time over 64 banks: the 16 rows
     // read at once land in 16 different bank groups)
@@ -465,6 +511,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     f32x4* sx = reinterpret_cast<f32x4*>(lds + C::NBUF * C::BUF);
     int32_t* seq_lds = reinterpret_cast<int32_t*>(lds + C::NBUF * C::BUF + C::SX);
     const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
+    uint8_t* stage = lds + C::NBUF * C::BUF + C::SX + C::SEQ;
+    int32_t* newp = reinterpret_cast<int32_t*>(stage + C::NBUF * C::STAGE);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int qg = lane >> 4;            // 4-row group of the MFMA layouts
@@ -513,7 +561,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
-            issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui, wave, lane);
+            issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui,
+                                 ki == ui.n - 1, stage + c * C::STAGE, newp + c, wave, lane);
             advance(a, st, U, ui, ki);
         }
     }
@@ -542,13 +591,38 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                     wait_vm<0>();
                 }
                 issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, j & 63),
-                                     lds + (j % C::NBUF) * C::BUF, ui, wave, lane);
+                                     lds + (j % C::NBUF) * C::BUF, ui, ki == ui.n - 1,
+                                     stage + (j % C::NBUF) * C::STAGE, newp + (j % C::NBUF), wave, lane);
                 advance(a, st, U, ui, ki);
             }
         }
         const uint8_t* kbuf = lds + (i % C::NBUF) * C::BUF;
         const uint8_t* vbuf = kbuf + C::PAGE;
         const int32_t t0 = (uc.page0 + kc) * kChunk;
+        if constexpr (!INT8) {
+            if (a.append && kc == uc.n - 1) {
+                // the new token (slot r of this page): patch its V values into
+                // the staged page before the value product reads them (the
+                // barrier after the scores orders it), and write its K row
+                // (already in LDS, from k_new) and V values to the slab
+                const int r = (uc.hi - 1) & 15;
+                const uint8_t* sg = stage + (i % C::NBUF) * C::STAGE;
+                const int64_t blk = ((int64_t)newp[i % C::NBUF] * a.hkv + uc.g) * C::PAGE;
+                uint8_t* vpatch = lds + (i % C::NBUF) * C::BUF + C::PAGE;
+                uint8_t* kdst = const_cast<uint8_t*>(a.k_slab) + blk + r * C::ROW;
+                uint8_t* vdst = const_cast<uint8_t*>(a.v_slab) + blk + r * 2;
+                for (int d = threadIdx.x; d < D; d += 256) {
+                    const uint16_t v = *reinterpret_cast<const uint16_t*>(sg + 2 * d);
+                    *reinterpret_cast<uint16_t*>(vpatch + d * 32 + ((((r >> 3) ^ (d >> 3)) & 1) << 4) + (r & 7) * 2) = v;
+                    *reinterpret_cast<uint16_t*>(vdst + d * 32) = v;
+                }
+                if (threadIdx.x < C::ROW / 16) {
+                    const int c = threadIdx.x;
+                    *reinterpret_cast<u32x4*>(kdst + c * 16) =
+                        *reinterpret_cast<const u32x4*>(kbuf + r * C::ROW + ((c ^ (r & 15)) * 16));
+                }
+            }
+        }
 
         // ---- partial scores over this wave's dim quarter --------------------
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -718,6 +792,9 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.arrivals = s.arrivals;
     a.part_o = s.part_o;
     a.part_ml = s.part_ml;
+    a.k_new = s.k_new;
+    a.v_new = s.v_new;
+    a.append = s.append;
     return a;
 }
 

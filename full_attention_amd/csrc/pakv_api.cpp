@@ -386,6 +386,43 @@ pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t la
     return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
 }
 
+pakv_status pakv_paged_attn_decode_append(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const void* plan, size_t plan_bytes, const void* k_new,
+                                          const void* v_new, const void* q, void* out,
+                                          int32_t num_seqs, int32_t max_kv_len,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
+    const auto& L = map->layers[layer];
+    const bool owner = L.source == layer;
+    if (owner && L.desc.kv_dtype != PAKV_KV_BF16)
+        return fail(PAKV_ERR_UNSUPPORTED, "append decode on an int8 layer is not built: store, then decode");
+    if (owner && num_seqs > 0 && (!k_new || !v_new)) return fail(PAKV_ERR_INVALID, "k_new or v_new is null");
+    DecodeLaunch a;
+    if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
+    if (num_seqs == 0) return PAKV_OK;
+    if (!q || !out) return fail(PAKV_ERR_INVALID, "q or out is null");
+    const auto& d = L.desc;
+    size_t need_plan = decode_plan_bytes(d, num_seqs, max_kv_len);
+    if (!plan || plan_bytes < need_plan)
+        return fail(PAKV_ERR_WORKSPACE, "decode plan needs %zu bytes, got %zu", need_plan,
+                    plan ? plan_bytes : (size_t)0);
+    size_t need = decode_partial_bytes(d, num_seqs);
+    if (!workspace || workspace_bytes < need)
+        return fail(PAKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.sched = const_cast<int32_t*>(static_cast<const int32_t*>(plan));
+    if (owner) {   // a shared layer's rows were stored by its source: a plain decode
+        a.k_new = static_cast<const uint16_t*>(k_new);
+        a.v_new = static_cast<const uint16_t*>(v_new);
+        a.append = 1;
+    }
+    bind_partials(a, workspace);
+    return hip_status(launch_decode(a, stream), "paged_attn_decode_append launch");
+}
+
 pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                    const int32_t* kv_lens, const void* q, void* out,
                                    int32_t num_seqs, int32_t max_kv_len,

@@ -111,6 +111,9 @@ struct DecodeLaunch {
     uint32_t* arrivals; // [units], zero between calls
     float* part_o;      // [grid + units][G][D]
     float* part_ml;     // [grid + units][G][2]
+    const uint16_t* k_new = nullptr;   // append: [num_seqs][hkv][D] bf16, stored at kv_len - 1
+    const uint16_t* v_new = nullptr;
+    int32_t append = 0;
 };
 int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
 int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched

@@ -31,6 +31,7 @@ EXPORTED = (
     "pakv_layer_map_bind_slab", "pakv_layer_map_source", "pakv_kv_bytes_per_token", "pakv_slab_bytes",
     "pakv_paged_kv_store", "pakv_decode_workspace_bytes", "pakv_paged_attn_decode",
     "pakv_decode_plan_bytes", "pakv_decode_plan", "pakv_paged_attn_decode_planned",
+    "pakv_paged_attn_decode_append",
     "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used",
 )
 
@@ -87,6 +88,9 @@ lib.pakv_decode_plan.restype = _I
 lib.pakv_decode_plan.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _I, _I, _P, _S, _P]
 lib.pakv_paged_attn_decode_planned.restype = _I
 lib.pakv_paged_attn_decode_planned.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _S, _P, _P, _I, _I, _P, _S, _P]
+lib.pakv_paged_attn_decode_append.restype = _I
+lib.pakv_paged_attn_decode_append.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _S, _P, _P, _P, _P, _I, _I, _P, _S,
+                                              _P]
 lib.pakv_paged_attn_extend.restype = _I
 lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
 lib.pakv_set_timing_events.restype = _I
@@ -218,6 +222,14 @@ def paged_attn_decode_planned(layer_map, layer, pages, plan, plan_bytes, q, out,
     return _check(lib.pakv_paged_attn_decode_planned(layer_map.handle, layer, ctypes.byref(pages), _ptr(plan),
                                                      plan_bytes, _ptr(q), _ptr(out), num_seqs, max_kv_len,
                                                      _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def paged_attn_decode_append(layer_map, layer, pages, plan, plan_bytes, k_new, v_new, q, out, num_seqs,
+                             max_kv_len, workspace, workspace_bytes, stream=None):
+    return _check(lib.pakv_paged_attn_decode_append(layer_map.handle, layer, ctypes.byref(pages), _ptr(plan),
+                                                    plan_bytes, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                                    num_seqs, max_kv_len, _ptr(workspace), workspace_bytes,
+                                                    _stream(stream)))
 
 
 def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_seqs, total_q, max_q_len,

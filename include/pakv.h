@@ -229,6 +229,29 @@ pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t la
                                            int32_t num_seqs, int32_t max_kv_len,
                                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Store, then decode, in one launch: the decode step of a layer whose new K/V
+ * row (one token per sequence) has not been stored yet.  The result and the
+ * slab afterwards are bit-identical to pakv_paged_kv_store of that row at
+ * position kv_lens[b] - 1 (cu_tokens = 0..num_seqs) followed by
+ * pakv_paged_attn_decode_planned with the same plan; the row is copied
+ * straight into the staged page of the workgroup that reads it, so the store
+ * costs no launch and no wait of its own.  (FreeToken PR #898: the store runs
+ * before attention in the forward, description, fourth bullet, and a store
+ * per layer per step is what its decode benchmark paragraph puts the shared
+ * layers' decode gain down to.)
+ *   k_new, v_new : device bf16 [num_seqs][Hkv][D], owned by the caller
+ *   plan         : from pakv_decode_plan for this step (it carries kv_lens)
+ * Other arguments as in pakv_paged_attn_decode_planned; kv_lens[b] must not
+ * exceed max_kv_len.  A shared layer stores nothing (its source's call stored
+ * the row) and k_new/v_new may be NULL: the call is then a planned decode.  An
+ * owning layer with int8 K/V returns PAKV_ERR_UNSUPPORTED before any launch
+ * (call pakv_paged_kv_store, then the planned decode). */
+pakv_status pakv_paged_attn_decode_append(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const void* plan, size_t plan_bytes, const void* k_new,
+                                          const void* v_new, const void* q, void* out,
+                                          int32_t num_seqs, int32_t max_kv_len,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked prefill: a chunk of new queries per sequence after a cached prefix.
  *   cu_q        : device int32 [num_seqs + 1], prefix sums of chunk lengths n_b
  *   prefix_lens : device int32 [num_seqs]; query i of sequence b sits at

@@ -219,6 +219,33 @@ def test_plan_argument_errors_are_returned_before_launch():
     assert lib.pakv_decode_plan(m.handle, 0, ctypes.byref(pages), None, 0, 40, None, 0, None) == pakv.OK
 
 
+def test_append_argument_errors_are_returned_before_launch():
+    """Every refusal of pakv_paged_attn_decode_append comes back on the host (no
+    GPU here: a launch would fail with PAKV_ERR_HIP instead)."""
+    m = _bound_map()           # 0: bf16 owner, 1: shared (source 0), 2: int8 owner
+    pages = pakv.Pages(0x5000, 2, 4)
+    lib = pakv.lib
+    need = lib.pakv_decode_plan_bytes(m.handle, 0, 2, 40)
+    ws = lib.pakv_decode_workspace_bytes(m.handle, 0, 2, 40)
+    f = lib.pakv_paged_attn_decode_append
+    P = ctypes.byref(pages)
+    # int8 owner: not built, whatever the other arguments
+    assert f(m.handle, 2, P, 0x9000, need, 0x6200, 0x6300, 0x6100, 0x7000, 2, 40, 0x8000, ws, None) == \
+        pakv.ERR_UNSUPPORTED
+    # bf16 owner without the new rows
+    assert f(m.handle, 0, P, 0x9000, need, None, 0x6300, 0x6100, 0x7000, 2, 40, 0x8000, ws, None) == pakv.ERR_INVALID
+    assert f(m.handle, 0, P, 0x9000, need, 0x6200, None, 0x6100, 0x7000, 2, 40, 0x8000, ws, None) == pakv.ERR_INVALID
+    # plan and workspace sizes, null q
+    assert f(m.handle, 0, P, 0x9000, need - 1, 0x6200, 0x6300, 0x6100, 0x7000, 2, 40, 0x8000, ws, None) == \
+        pakv.ERR_WORKSPACE
+    assert f(m.handle, 0, P, 0x9000, need, 0x6200, 0x6300, 0x6100, 0x7000, 2, 40, 0x8000, 16, None) == \
+        pakv.ERR_WORKSPACE
+    assert f(m.handle, 0, P, 0x9000, need, 0x6200, 0x6300, None, 0x7000, 2, 40, 0x8000, ws, None) == pakv.ERR_INVALID
+    # a shared layer needs no new rows; no sequences: nothing to do
+    assert f(m.handle, 1, P, 0x9000, need, None, None, None, 0x7000, 2, 40, 0x8000, ws, None) == pakv.ERR_INVALID
+    assert f(m.handle, 0, P, None, 0, None, None, None, None, 0, 40, None, 0, None) == pakv.OK
+
+
 def test_too_many_sequences_or_units_per_decode_call_are_refused():
     m = pakv.LayerMap([_desc(hq=16, hkv=8)])
     m.bind_slab(0, 0x1000, 0x2000, 8)
