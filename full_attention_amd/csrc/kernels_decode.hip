@@ -96,7 +96,11 @@ struct Cfg {
     static constexpr int PAGE = 16 * D * ES;                // bytes per (page, head) block
     static constexpr int SCALE_BYTES = INT8 ? 128 : 0;      // k and v scales of one page
     static constexpr int BUF = 2 * PAGE + SCALE_BYTES;
-    static constexpr int NBUF = (D == 512 && !INT8) ? 2 : 4;
+    // ring slots: bf16 pages copied one ahead (two slots); a deeper ring
+    // (three or four slots at D = 256) was slower in the step: with every
+    // workgroup streaming, more requests in flight only lengthen the queues
+    // and the stragglers.  int8 pages are half the bytes: four slots.
+    static constexpr int NBUF = INT8 ? 4 : 2;
     static constexpr int KV_DMA = 2 * PAGE / (1024 * kWaves);   // copies per wave per chunk
     static constexpr int PER = KV_DMA + (INT8 ? 1 : 0);
     static constexpr int SX = kWaves * 64 * 16;             // partial-score exchange
