@@ -436,19 +436,64 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
     return *ticket == expected - 1;
 }
 
+// One batch of a unit's merge: partial slots sl0, sl0 + G, ... (CNT of them,
+// in workgroup order) folded into (M, L, acc).  All loads are issued before
+// the first wait, and exactly CNT partials are read: the batch size is a
+// template argument, so the last, partial batch of a unit neither loads
+// padding nor holds registers whose definition depends on a branch (the loads
+// are asynchronous, and a value merged from two branches could be copied
+// before it lands).
+template <int D, int CNT>
+__device__ __forceinline__ void merge_batch(const float* o_base, const float* ml_base, uint32_t sl0, int32_t G,
+                                            int d0, float& M, float& L, f32x4 (&acc)[D / 128]) {
+    constexpr int IPT = D / 128;
+    f32x2 ml[CNT];
+    f32x4 ov[CNT * IPT];
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) {
+        const uint32_t sl = sl0 + (uint32_t)(k * G);
+        ml[k] = get2s(ml_base, sl * 8u);
+        const uint32_t ob = (sl * D + d0) * 4u;
+        ov[k * IPT + 0] = get4s<0>(o_base, ob);
+        ov[k * IPT + 1] = get4s<512>(o_base, ob);
+        if constexpr (IPT > 2) {
+            ov[k * IPT + 2] = get4s<1024>(o_base, ob);
+            ov[k * IPT + 3] = get4s<1536>(o_base, ob);
+        }
+    }
+    await(ml);
+    await(ov);
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) Mb = fmaxf(Mb, ml[k].x);
+    const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
+    const float r = exp2f(M - Mb_use);            // rescale what came before
+    L *= r;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) acc[j] *= r;
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) {
+        const float wt = exp2f(ml[k].x - Mb_use);
+        L += wt * ml[k].y;
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) acc[j] += wt * ov[k * IPT + j];
+    }
+    M = Mb;
+}
+
 // Merges the partials of unit x (slots w + x.u for w in [w0, w1], in that
 // order) and writes the G heads' bf16 outputs.  Thread t owns IPT = D/128
 // 4-dim items of one head, dims 4 (t % 32) + 128 j, so one (m, l) pair per
 // partial serves all of them while each load instruction still reads 512
-// contiguous bytes per head; a pass covers 8 heads.  Each batch issues all its loads before
-// the first wait: a unit of up to BATCH partials is merged in one round trip
-// (the merging workgroup's own bandwidth bounds it, so fewer, fuller round
-// trips are what shorten it).
+// contiguous bytes per head; a pass covers 8 heads.  Partials go in batches
+// of BATCH (all loads of a batch in flight together): the merging
+// workgroup's own bandwidth bounds the merge, so the batches carry no
+// padding.
 template <int D>
 __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
     constexpr int IPT = D / 128;
     constexpr int TPH = (D / 4) / IPT;                 // threads per head (32)
-    constexpr int BATCH = (D == 512) ? 7 : 12;
+    constexpr int BATCH = (D == 512) ? 7 : 8;
     static_assert(IPT == 2 || IPT == 4, "items per thread");
     const int d0 = (t % TPH) * 4;
     // byte offsets below are 32-bit: the partial buffers are sized by the
@@ -462,41 +507,60 @@ __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32
         f32x4 acc[IPT];
 #pragma unroll
         for (int j = 0; j < IPT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int32_t wb = w0; wb <= w1; wb += BATCH) {
-            f32x2 ml[BATCH];
-            f32x4 ov[BATCH * IPT];
+        if constexpr (D == 256) {
+            int32_t wb = w0;
+            for (; wb + BATCH - 1 <= w1; wb += BATCH)
+                merge_batch<D, BATCH>(o_base, ml_base, (uint32_t)((wb + x.u) * G + hl), G, d0, M, L, acc);
+            const uint32_t sl0 = (uint32_t)((wb + x.u) * G + hl);
+            switch (w1 - wb + 1) {    // the rest, 0 .. BATCH - 1 partials, without padding
+                case 1: merge_batch<D, 1>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 2: merge_batch<D, 2>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 3: merge_batch<D, 3>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 4: merge_batch<D, 4>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 5: merge_batch<D, 5>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 6: merge_batch<D, 6>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 7: merge_batch<D, 7>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                default: break;
+            }
+        } else {
+            // D = 512: one batch body for every batch, the last one padded by
+            // re-reading slot w1 with weight zero (the exact-count form's extra
+            // code cost this kernel more than the padding does)
+            for (int32_t wb = w0; wb <= w1; wb += BATCH) {
+                f32x2 ml[BATCH];
+                f32x4 ov[BATCH * IPT];
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k) {
-                const uint32_t sl = (uint32_t)((min(wb + k, w1) + x.u) * G + hl);
-                ml[k] = get2s(ml_base, sl * 8u);
-                const uint32_t ob = (sl * D + d0) * 4u;
-                ov[k * IPT + 0] = get4s<0>(o_base, ob);
-                ov[k * IPT + 1] = get4s<512>(o_base, ob);
-                if constexpr (IPT > 2) {
-                    ov[k * IPT + 2] = get4s<1024>(o_base, ob);
-                    ov[k * IPT + 3] = get4s<1536>(o_base, ob);
+                for (int k = 0; k < BATCH; ++k) {
+                    const uint32_t sl = (uint32_t)((min(wb + k, w1) + x.u) * G + hl);
+                    ml[k] = get2s(ml_base, sl * 8u);
+                    const uint32_t ob = (sl * D + d0) * 4u;
+                    ov[k * IPT + 0] = get4s<0>(o_base, ob);
+                    ov[k * IPT + 1] = get4s<512>(o_base, ob);
+                    if constexpr (IPT > 2) {
+                        ov[k * IPT + 2] = get4s<1024>(o_base, ob);
+                        ov[k * IPT + 3] = get4s<1536>(o_base, ob);
+                    }
                 }
+                await(ml);
+                await(ov);
+                float Mb = M;
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k)
+                    if (wb + k <= w1) Mb = fmaxf(Mb, ml[k].x);
+                const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
+                const float r = exp2f(M - Mb_use);            // rescale what came before
+                L *= r;
+#pragma unroll
+                for (int j = 0; j < IPT; ++j) acc[j] *= r;
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) {
+                    const float wt = (wb + k <= w1) ? exp2f(ml[k].x - Mb_use) : 0.0f;
+                    L += wt * ml[k].y;
+#pragma unroll
+                    for (int j = 0; j < IPT; ++j) acc[j] += wt * ov[k * IPT + j];
+                }
+                M = Mb;
             }
-            await(ml);
-            await(ov);
-            float Mb = M;
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k)
-                if (wb + k <= w1) Mb = fmaxf(Mb, ml[k].x);
-            const float Mb_use = (Mb == -INFINITY) ? 0.0f : Mb;
-            const float r = exp2f(M - Mb_use);            // rescale what came before
-            L *= r;
-#pragma unroll
-            for (int j = 0; j < IPT; ++j) acc[j] *= r;
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k) {
-                // slots past w1 repeat w1's (finite) partial with weight zero
-                const float wt = (wb + k <= w1) ? exp2f(ml[k].x - Mb_use) : 0.0f;
-                L += wt * ml[k].y;
-#pragma unroll
-                for (int j = 0; j < IPT; ++j) acc[j] += wt * ov[k * IPT + j];
-            }
-            M = Mb;
         }
         const float inv = 1.0f / L;
         uint16_t* op = a.out + ((int64_t)x.b * a.hq + (int64_t)x.g * G + hl) * D + d0;
