@@ -211,26 +211,101 @@ __device__ __forceinline__ uint32_t page_of_chunk(const DecodeArgs& a, const int
     return ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : 0u;
 }
 
+// Prefix over sequences of the decode workgroups an aligned split gives them
+// (ws[b]; ws[B] = total): every unit of sequence b, n_b chunks, gets
+// ceil(n_b / per) workgroups, so that no run crosses a unit.
+__device__ __forceinline__ void build_wg_table(const DecodeArgs& a, const SeqTable& st, int32_t B, int32_t per,
+                                               int32_t* ws) {
+    __shared__ int32_t wave_tot[kWaves];
+    const int t = threadIdx.x;
+    const int per_t = (B + 255) / 256;
+    const int b0 = t * per_t, b1 = min(b0 + per_t, B);
+    int32_t local = 0;
+    for (int b = b0; b < b1; ++b) local += a.hkv * ((chunks_of(a, st.slen[b]) + per - 1) / per);
+    int32_t incl = local;
+    const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    int32_t run = before + incl - local;
+    for (int b = b0; b < b1; ++b) {
+        ws[b] = run;
+        run += a.hkv * ((chunks_of(a, st.slen[b]) + per - 1) / per);
+    }
+    if (t == 255) ws[B] = before + incl;
+    __syncthreads();
+}
+
 // The schedule of a decode call (the plan): every workgroup of the plan
 // kernel builds the sequence table, takes the run of the chunk stream that
-// decode workgroup blockIdx.x will take (equal contiguous runs of
-// ceil(T / grid) chunks) and writes its record and the page ids of its
-// chunks; workgroup 0 also writes the header and the table.
+// decode workgroup blockIdx.x will take and writes its record and the page
+// ids of its chunks; workgroup 0 also writes the header and the table.
+//
+// Runs hold at most per = ceil(T / grid) chunks.  When giving every unit its
+// own ceil(n / per) workgroups fits the grid (as it does when units are few
+// and of similar length, like a sliding window's), each unit is split evenly
+// over its own workgroups and no run crosses a unit: a run that crosses one
+// writes two partials and reloads Q in mid-stream, and those workgroups were
+// the last to finish.  Otherwise runs are equal contiguous pieces of the
+// stream (stream-K).  Record fields: c_begin, c_end, first unit, its first
+// chunk, then per for stream-K, or 0 and the first and last workgroup of the
+// unit for the aligned split.
 __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
                                                            const int32_t* __restrict__ kv_lens) {
     __shared__ int32_t seq_lds[2 * (pakv::kDecodeMaxSeqs + 1)];
+    __shared__ int32_t ws_lds[pakv::kDecodeMaxSeqs + 1];
     const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
     const int t = threadIdx.x;
     const int32_t B = a.num_seqs;
     build_seq_table(a, kv_lens, st, B);
     const int32_t T = st.soff[B];
-    const int32_t per = (T + a.grid - 1) / a.grid;
-    const int32_t c_begin = min((int32_t)blockIdx.x * per, T);
-    const int32_t c_end = min(c_begin + per, T);
+    const int32_t per = max((T + a.grid - 1) / a.grid, 1);
+    build_wg_table(a, st, B, per, ws_lds);
+    const bool aligned = ws_lds[B] <= a.grid;
+    const int32_t w = blockIdx.x;
+    int32_t c_begin, c_end, u = 0, kc = 0, rw0 = 0, rw1 = 0;
+    if (aligned) {
+        c_begin = c_end = T;
+        if (w < ws_lds[B]) {
+            int32_t lo = 0, hi = B - 1;                 // sequence b: the last with ws[b] <= w
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (ws_lds[mid] <= w) lo = mid; else hi = mid - 1;
+            }
+            const int32_t b = lo;
+            const int32_t n = chunks_of(a, st.slen[b]);
+            const int32_t nw = (n + per - 1) / per;     // workgroups per unit of b
+            const int32_t r = w - ws_lds[b], g = r / nw, k = r % nw;
+            const int32_t first = st.soff[b] + g * n;
+            u = b * a.hkv + g;
+            kc = (k * n) / nw;
+            c_begin = first + kc;
+            c_end = first + ((k + 1) * n) / nw;
+            rw0 = ws_lds[b] + g * nw;
+            rw1 = rw0 + nw - 1;
+        }
+    } else {
+        c_begin = min(w * per, T);
+        c_end = min(c_begin + per, T);
+        if (c_begin < c_end) {
+            const int32_t b = seq_of_chunk(st, B, c_begin);
+            const int32_t n = chunks_of(a, st.slen[b]);
+            const int32_t r = c_begin - st.soff[b];
+            u = b * a.hkv + r / n;
+            kc = r % n;
+        }
+    }
     int32_t* S = a.sched;
     if (blockIdx.x == 0) {
         if (t == 0) {
-            const int32_t head[8] = {pakv::kPlanMagic, T, per, a.grid, B, a.hkv, a.window, a.max_kv_len};
+            const int32_t head[8] = {pakv::kPlanMagic, T, aligned ? 0 : per, a.grid, B, a.hkv, a.window,
+                                     a.max_kv_len};
 #pragma unroll
             for (int i = 0; i < 8; ++i) S[i] = head[i];
         }
@@ -239,19 +314,13 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
     }
     int32_t* rec = S + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
     if (t == 0) {
-        int32_t u = 0, kc = 0;
-        if (c_begin < c_end) {
-            const int32_t b = seq_of_chunk(st, B, c_begin);
-            const int32_t n = chunks_of(a, st.slen[b]);
-            const int32_t r = c_begin - st.soff[b];
-            u = b * a.hkv + r / n;
-            kc = r % n;
-        }
         rec[0] = c_begin;
         rec[1] = c_end;
         rec[2] = u;
         rec[3] = kc;
-        rec[4] = per;
+        rec[4] = aligned ? 0 : per;
+        rec[5] = rw0;
+        rec[6] = rw1;
     }
     for (int32_t j = t; j < max(c_end - c_begin, 64); j += 256) {
         const bool in_run = c_begin + j < c_end;
@@ -613,7 +682,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int32_t c_end = (int32_t)min((int64_t)__builtin_amdgcn_readlane(field, 1), a.s_cap);
     const int32_t u_first = clamp_i32(__builtin_amdgcn_readlane(field, 2), 0, U - 1);
     const int32_t kc_first = max(__builtin_amdgcn_readlane(field, 3), 0);
-    const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 1);
+    // stream-K runs (per > 0) or unit-aligned runs (per = 0; the unit's
+    // workgroups are [rw0, rw1], clamped so that a stale plan stays in bounds)
+    const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 0);
+    const int32_t rw0 = clamp_i32(__builtin_amdgcn_readlane(field, 5), 0, (int32_t)blockIdx.x);
+    const int32_t rw1 = clamp_i32(__builtin_amdgcn_readlane(field, 6), (int32_t)blockIdx.x, a.grid - 1);
     ids = (ids < (uint32_t)a.num_pages) ? ids : 0u;
     __syncthreads();
     if (c_begin >= c_end) return;
@@ -785,7 +858,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         // ---- end of this run's part of the unit --------------------------------
         if (kc == uc.n - 1 || i == total - 1) {
             const float l_tot = wave_sum_across_groups(l_run);
-            const int32_t w0 = uc.first / per, w1 = (uc.first + uc.n - 1) / per;
+            const int32_t w0 = per > 0 ? uc.first / per : rw0;
+            const int32_t w1 = per > 0 ? (uc.first + uc.n - 1) / per : rw1;
             if (w0 == w1) {
                 // the whole unit is in this run: normalise and write the outputs
                 if (col < G) {
