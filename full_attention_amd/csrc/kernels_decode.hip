@@ -1,12 +1,14 @@
 // paged_attn_decode: split-KV decode with a deterministic combine.
 //
-// Pass 1 (partial), stream-K: the work of all (sequence b, KV head g) units
-// is a stream of 16-token chunks (one page each): unit (b, g) covers the
-// pages that hold its visible keys [lo, L).  A fixed grid of kGrid persistent
-// workgroups (4 wavefronts each) takes equal, contiguous runs of that stream,
-// so every workgroup moves the same number of bytes whatever the length mix.
-// A run that crosses unit boundaries produces one partial (o, m, l) per unit
-// it touches, stored at slot (workgroup + unit).  Chunks are streamed into
+// Pass 1 (partial): the work of all (sequence b, KV head g) units is a
+// stream of 16-token chunks (one page each): unit (b, g) covers the pages
+// that hold its visible keys [lo, L).  A fixed grid of persistent workgroups
+// (4 wavefronts each) takes contiguous runs of that stream of at most a
+// common length: split unit by unit when every unit can have workgroups of
+// its own (no run then crosses a unit), else equal pieces of the stream
+// (stream-K), so every workgroup moves about the same bytes whatever the
+// length mix.  A run that crosses unit boundaries produces one partial
+// (o, m, l) per unit it touches, stored at slot (workgroup + unit).  Chunks are streamed into
 // LDS by asynchronous global->LDS copies (global_load_lds_dwordx4), NBUF deep,
 // so the bytes in flight hold no registers.  For each chunk:
 //

@@ -40,14 +40,16 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
 // words written by the plan kernel from kv_lens and the page table and read by
 // the decode kernel, so that a decode workgroup learns its run of the chunk
 // stream and the first page ids in one load:
-//   [0, kPlanHeader)   magic, total chunks T, chunks per workgroup, grid, B,
-//                      Hkv, window, max_kv_len
+//   [0, kPlanHeader)   magic, total chunks T, chunks per workgroup (0 for
+//                      the unit-aligned split), grid, B, Hkv, window, max_kv_len
 //   soff [B + 1]       first stream chunk of each sequence's units; soff[B] = T
 //   slen [B]           length of each sequence, clamped to [1, max_kv_len]
 //   rec  [grid][kPlanRecord]  per workgroup: first chunk, end chunk, unit of
 //                      the first chunk, that chunk's index in its unit, chunks
-//                      per workgroup, spare words, then from word kPlanRecIds
-//                      the page ids of its first 64 chunks (0 past its run)
+//                      per workgroup (0 for the unit-aligned split), the first
+//                      and last workgroup of its unit (aligned split only),
+//                      spare words, then from word kPlanRecIds the page ids of
+//                      its first 64 chunks (0 past its run)
 //   ids  [cap]         page id of every stream chunk (ids outside the pool
 //                      already replaced by 0)
 constexpr int32_t kPlanMagic = 0x31504b50;

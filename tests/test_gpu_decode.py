@@ -268,3 +268,66 @@ def test_planned_decode_in_graph_replays():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), f"replay {rep} differs"
+
+
+def _read_plan(plan, B, max_kv_len, hkv=1):
+    """Header and per-workgroup records of a decode plan (the schedule layout the
+    plan and decode kernels share; grid 512)."""
+    w = plan.cpu().numpy().view(np.int32)
+    soff, slen = 16, 16 + B + 1
+    rec = (slen + B + 15) & ~15
+    head = w[:8]
+    recs = w[rec:rec + 512 * 80].reshape(512, 80)[:, :7]
+    return head, recs, w[soff:soff + B + 1], w[slen:slen + B]
+
+
+@pytest.mark.parametrize("case", ["sliding", "full", "skewed"])
+def test_plan_runs_partition_the_stream(case):
+    """The plan's runs cover the key stream once, in workgroup order, none longer
+    than the chunks-per-workgroup bound plus an eighth; with the unit-aligned
+    split (chosen when every unit can have its own workgroups) no run crosses a
+    unit and each unit's record names exactly the workgroups that cover it."""
+    need_gpu()
+    from workloads import e2b_decode_workload
+    rng = np.random.default_rng(5)
+    if case == "skewed":
+        lens = [100000] + [20] * 700
+        window = 0
+    else:
+        lens = list(np.array(e2b_decode_workload().cached_lens) + 1)
+        window = 512 if case == "sliding" else 0
+    spec = LayerSpec("sliding" if window else "full", 256, 8, 1, window)
+    from full_attention_amd.cache import PagedKVCache
+    from workloads import make_page_pool
+    pool = make_page_pool(rng, lens)
+    cache = PagedKVCache([spec], None, pool.num_pages, sentinel=False)
+    cache.set_page_table(pool.page_table)
+    B, maxl = len(lens), max(lens)
+    plan = cache.decode_plan(0, i32(lens), maxl)
+    torch.cuda.synchronize()
+    head, recs, soff, slen = _read_plan(plan, B, maxl)
+    T = int(head[1])
+    L = np.array(lens)
+    lo = np.maximum(0, L - window) if window else np.zeros(B, np.int64)
+    n = (L + 15) // 16 - lo // 16
+    assert T == int(n.sum()) and soff[B] == T
+    per0 = -(-T // 512)
+    cb, ce = recs[:, 0], recs[:, 1]
+    busy = cb < ce
+    # cover [0, T) exactly once, in workgroup order
+    order = np.argsort(cb[busy], kind="stable")
+    assert np.all(order == np.arange(busy.sum()))
+    starts, ends = cb[busy], ce[busy]
+    assert starts[0] == 0 and ends[-1] == T and np.all(starts[1:] == ends[:-1])
+    aligned = head[2] == 0
+    assert aligned == (case != "skewed")
+    longest = int((ends - starts).max())
+    assert longest <= (per0 + max(per0 // 8, 1) if aligned else per0)
+    if aligned:
+        unit_first = soff[:B]                         # one KV head: unit b starts at soff[b]
+        for wg in np.nonzero(busy)[0]:
+            c0, c1, u, kc, per, w0, w1 = (int(x) for x in recs[wg])
+            assert per == 0 and w0 <= wg <= w1
+            assert c0 - unit_first[u] == kc and c1 <= unit_first[u] + n[u]       # inside its unit
+            assert all(recs[x, 2] == u for x in range(w0, w1 + 1))               # the unit's workgroups
+            assert recs[w0, 0] == unit_first[u] and recs[w1, 1] == unit_first[u] + n[u]
