@@ -384,9 +384,10 @@ __device__ __forceinline__ void take_q(u32x4 (&qreg)[N], bool real) {
 // that owns it copies from k_new instead (same swizzle, so no two copies
 // write the same LDS bytes), and wave 0 first stages the new V row (the V page
 // is dim-major: the new token is two bytes in every 32) for the consumer to
-// patch in.  Every wave still issues at least PER copies for the chunk, and
-// the staging copy comes before them, so the per-chunk waits still cover
-// everything (they can only wait for one copy more than needed).
+// patch in.  Every wave still issues at least PER / 2 copies of K and then
+// PER / 2 of V for the chunk, and the staging copy comes before them, so the
+// waits for a chunk's K and for its V still cover everything (they can only
+// wait for one copy more than needed).
 template <int D, bool INT8>
 __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, uint8_t* buf, const Unit& x,
                                             bool last, uint8_t* stage, int32_t* newp, int wave, int lane) {
@@ -728,7 +729,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     for (int32_t i = 0; i < total; ++i) {
-        wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
+        // bf16: this chunk's K only (each wave issues K before V); its V is
+        // awaited after the scores, so the score product overlaps V's arrival
+        if constexpr (!INT8) wait_vm<C::PER / 2>();
+        else wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
         lds_barrier();
         if (kc == 0 || i == 0) {
             // a new unit: its Q.  The first was issued before chunk 0's copies,
@@ -756,21 +760,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         const int32_t t0 = (uc.page0 + kc) * kChunk;
         if constexpr (!INT8) {
             if (a.append && kc == uc.n - 1) {
-                // the new token (slot r of this page): patch its V values into
-                // the staged page before the value product reads them (the
-                // barrier after the scores orders it), and write its K row
-                // (already in LDS, from k_new) and V values to the slab
+                // the new token (slot r of this page): write its K row (already
+                // in LDS, from k_new) and its staged V values to the slab; the V
+                // values are patched into the staged page once its copies have
+                // landed (after the score exchange)
                 const int r = (uc.hi - 1) & 15;
                 const uint8_t* sg = stage + (i % C::NBUF) * C::STAGE;
                 const int64_t blk = ((int64_t)newp[i % C::NBUF] * a.hkv + uc.g) * C::PAGE;
-                uint8_t* vpatch = lds + (i % C::NBUF) * C::BUF + C::PAGE;
                 uint8_t* kdst = const_cast<uint8_t*>(a.k_slab) + blk + r * C::ROW;
                 uint8_t* vdst = const_cast<uint8_t*>(a.v_slab) + blk + r * 2;
-                for (int d = threadIdx.x; d < D; d += 256) {
-                    const uint16_t v = *reinterpret_cast<const uint16_t*>(sg + 2 * d);
-                    *reinterpret_cast<uint16_t*>(vpatch + d * 32 + ((((r >> 3) ^ (d >> 3)) & 1) << 4) + (r & 7) * 2) = v;
-                    *reinterpret_cast<uint16_t*>(vdst + d * 32) = v;
-                }
+                for (int d = threadIdx.x; d < D; d += 256)
+                    *reinterpret_cast<uint16_t*>(vdst + d * 32) = *reinterpret_cast<const uint16_t*>(sg + 2 * d);
                 if (threadIdx.x < C::ROW / 16) {
                     const int c = threadIdx.x;
                     *reinterpret_cast<u32x4*>(kdst + c * 16) =
@@ -798,8 +798,27 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                 acc = mfma_16x16x32(ka, qreg[kk], acc);
             }
         }
+        if constexpr (!INT8) {
+            // this chunk's V: past it, only the next chunk's copies (issued at
+            // the top of this step) may still be in flight
+            if (i + 1 < total) wait_vm<C::PER>();
+            else wait_vm<0>();
+        }
         sx[wave * 64 + lane] = acc;
         lds_barrier();
+        if constexpr (!INT8) {
+            if (a.append && kc == uc.n - 1) {
+                // every wave's V copies have landed: patch in the new token's V
+                // (two bytes per dim, each dim's 32 bytes copied by one wave)
+                const int r = (uc.hi - 1) & 15;
+                const uint8_t* sg = stage + (i % C::NBUF) * C::STAGE;
+                uint8_t* vpatch = lds + (i % C::NBUF) * C::BUF + C::PAGE;
+                for (int d = threadIdx.x; d < D; d += 256)
+                    *reinterpret_cast<uint16_t*>(vpatch + d * 32 + ((((r >> 3) ^ (d >> 3)) & 1) << 4) + (r & 7) * 2) =
+                        *reinterpret_cast<const uint16_t*>(sg + 2 * d);
+                lds_barrier();
+            }
+        }
         f32x4 tot = sx[lane];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) tot += sx[w * 64 + lane];
