@@ -731,6 +731,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     for (int32_t i = 0; i < total; ++i) {
         // bf16: this chunk's K only (each wave issues K before V); its V is
         // awaited after the scores, so the score product overlaps V's arrival
+        // (with one chunk ahead, only this chunk's copies are in flight here)
+        static_assert(INT8 || C::NBUF == 2, "the split K / V waits count one chunk in flight");
         if constexpr (!INT8) wait_vm<C::PER / 2>();
         else wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
         lds_barrier();
