@@ -28,7 +28,11 @@
 //
 // Combine: the workgroup that finishes a unit's last partial (a per-unit
 // arrival counter; the merging workgroup resets it to zero) merges the unit's
-// partials in workgroup order: M = max_s m_s,
+// partials.  The dispatcher places workgroup i on XCD i mod 8 (the same class
+// of i mod 8 shares an XCD also when a partition has 1, 2 or 4 XCDs), and the
+// plan's workgroup numbering gives each XCD a contiguous block of runs; a
+// unit whose runs all fall in one block exchanges its partials through that
+// XCD's L2, the others through memory.  The merge goes in workgroup order: M = max_s m_s,
 // O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, rounded to bf16.  Which
 // workgroup merges does not change the arithmetic, no atomics touch
 // floating-point data, and the partition depends only on the lengths, so
@@ -473,33 +477,37 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
 //   the MFMA; mfma_settle() (24 wait states, more than any MFMA here needs)
 //   separates the value product from the put4s that store its output.
 __device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// Partial exchange.  Device scope (sc1): the partials and the counter go
+// through memory, for units whose workgroups sit on different XCDs.  Local:
+// every workgroup of the unit is on one XCD, whose L2 all its CUs share, so
+// stores stop in that L2 (the vector L1 writes through), the counter's atomic
+// runs there, and loads skip only the L1 (sc0).
+template <bool LOCAL>
 __device__ __forceinline__ void put4(float* p, f32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
+    if constexpr (LOCAL) asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
+    else asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
+template <bool LOCAL>
 __device__ __forceinline__ void put2(float* p, float x, float y) {
-    asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(f32x2{x, y}) : "memory");
-}
-__device__ __forceinline__ f32x4 get4(const float* p) {
-    f32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
-__device__ __forceinline__ f32x2 get2(const float* p) {
-    f32x2 v;
-    asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-    return v;
+    if constexpr (LOCAL) asm volatile("global_store_dwordx2 %0, %1, off" : : "v"(p), "v"(f32x2{x, y}) : "memory");
+    else asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(f32x2{x, y}) : "memory");
 }
 // Scalar base + 32-bit byte offset forms: one address VGPR per partial
 // serves all of a thread's items through the immediate offset.
-template <int OFF>
+template <bool LOCAL, int OFF>
 __device__ __forceinline__ f32x4 get4s(const float* base, uint32_t voff) {
     f32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 sc1" : "=v"(v) : "v"(voff), "s"(base), "i"(OFF) : "memory");
+    if constexpr (LOCAL)
+        asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 sc0" : "=v"(v) : "v"(voff), "s"(base), "i"(OFF) : "memory");
+    else
+        asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 sc1" : "=v"(v) : "v"(voff), "s"(base), "i"(OFF) : "memory");
     return v;
 }
+template <bool LOCAL>
 __device__ __forceinline__ f32x2 get2s(const float* base, uint32_t voff) {
     f32x2 v;
-    asm volatile("global_load_dwordx2 %0, %1, %2 sc1" : "=v"(v) : "v"(voff), "s"(base) : "memory");
+    if constexpr (LOCAL) asm volatile("global_load_dwordx2 %0, %1, %2 sc0" : "=v"(v) : "v"(voff), "s"(base) : "memory");
+    else asm volatile("global_load_dwordx2 %0, %1, %2 sc1" : "=v"(v) : "v"(voff), "s"(base) : "memory");
     return v;
 }
 template <int N, typename T>
@@ -511,11 +519,16 @@ __device__ __forceinline__ void await(T (&regs)[N]) {
 
 // Counts this workgroup's arrival at a unit and reports whether it was the
 // last of `expected` (then every partial of the unit is complete).
+template <bool LOCAL>
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* ticket) {
     wait_vm<0>();               // this wave's partial stores are complete
     lds_barrier();              // ... and every wave's
-    if (threadIdx.x == 0)
-        *ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        if constexpr (LOCAL)
+            *ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            *ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     lds_barrier();
     return *ticket == expected - 1;
 }
@@ -527,7 +540,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 // padding nor holds registers whose definition depends on a branch (the loads
 // are asynchronous, and a value merged from two branches could be copied
 // before it lands).
-template <int D, int CNT>
+template <int D, int CNT, bool LOCAL>
 __device__ __forceinline__ void merge_batch(const float* o_base, const float* ml_base, uint32_t sl0, int32_t G,
                                             int d0, float& M, float& L, f32x4 (&acc)[D / 128]) {
     constexpr int IPT = D / 128;
@@ -536,13 +549,13 @@ __device__ __forceinline__ void merge_batch(const float* o_base, const float* ml
 #pragma unroll
     for (int k = 0; k < CNT; ++k) {
         const uint32_t sl = sl0 + (uint32_t)(k * G);
-        ml[k] = get2s(ml_base, sl * 8u);
+        ml[k] = get2s<LOCAL>(ml_base, sl * 8u);
         const uint32_t ob = (sl * D + d0) * 4u;
-        ov[k * IPT + 0] = get4s<0>(o_base, ob);
-        ov[k * IPT + 1] = get4s<512>(o_base, ob);
+        ov[k * IPT + 0] = get4s<LOCAL, 0>(o_base, ob);
+        ov[k * IPT + 1] = get4s<LOCAL, 512>(o_base, ob);
         if constexpr (IPT > 2) {
-            ov[k * IPT + 2] = get4s<1024>(o_base, ob);
-            ov[k * IPT + 3] = get4s<1536>(o_base, ob);
+            ov[k * IPT + 2] = get4s<LOCAL, 1024>(o_base, ob);
+            ov[k * IPT + 3] = get4s<LOCAL, 1536>(o_base, ob);
         }
     }
     await(ml);
@@ -573,7 +586,7 @@ __device__ __forceinline__ void merge_batch(const float* o_base, const float* ml
 // of BATCH (all loads of a batch in flight together): the merging
 // workgroup's own bandwidth bounds the merge, so the batches carry no
 // padding.
-template <int D>
+template <int D, bool LOCAL>
 __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
     constexpr int IPT = D / 128;
     constexpr int TPH = (D / 4) / IPT;                 // threads per head (32)
@@ -594,16 +607,16 @@ __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32
         if constexpr (D == 256) {
             int32_t wb = w0;
             for (; wb + BATCH - 1 <= w1; wb += BATCH)
-                merge_batch<D, BATCH>(o_base, ml_base, (uint32_t)((wb + x.u) * G + hl), G, d0, M, L, acc);
+                merge_batch<D, BATCH, LOCAL>(o_base, ml_base, (uint32_t)((wb + x.u) * G + hl), G, d0, M, L, acc);
             const uint32_t sl0 = (uint32_t)((wb + x.u) * G + hl);
             switch (w1 - wb + 1) {    // the rest, 0 .. BATCH - 1 partials, without padding
-                case 1: merge_batch<D, 1>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 2: merge_batch<D, 2>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 3: merge_batch<D, 3>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 4: merge_batch<D, 4>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 5: merge_batch<D, 5>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 6: merge_batch<D, 6>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
-                case 7: merge_batch<D, 7>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 1: merge_batch<D, 1, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 2: merge_batch<D, 2, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 3: merge_batch<D, 3, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 4: merge_batch<D, 4, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 5: merge_batch<D, 5, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 6: merge_batch<D, 6, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
+                case 7: merge_batch<D, 7, LOCAL>(o_base, ml_base, sl0, G, d0, M, L, acc); break;
                 default: break;
             }
         } else {
@@ -616,13 +629,13 @@ __device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32
 #pragma unroll
                 for (int k = 0; k < BATCH; ++k) {
                     const uint32_t sl = (uint32_t)((min(wb + k, w1) + x.u) * G + hl);
-                    ml[k] = get2s(ml_base, sl * 8u);
+                    ml[k] = get2s<LOCAL>(ml_base, sl * 8u);
                     const uint32_t ob = (sl * D + d0) * 4u;
-                    ov[k * IPT + 0] = get4s<0>(o_base, ob);
-                    ov[k * IPT + 1] = get4s<512>(o_base, ob);
+                    ov[k * IPT + 0] = get4s<LOCAL, 0>(o_base, ob);
+                    ov[k * IPT + 1] = get4s<LOCAL, 512>(o_base, ob);
                     if constexpr (IPT > 2) {
-                        ov[k * IPT + 2] = get4s<1024>(o_base, ob);
-                        ov[k * IPT + 3] = get4s<1536>(o_base, ob);
+                        ov[k * IPT + 2] = get4s<LOCAL, 1024>(o_base, ob);
+                        ov[k * IPT + 3] = get4s<LOCAL, 1536>(o_base, ob);
                     }
                 }
                 await(ml);
@@ -677,7 +690,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // the page ids of its first 64 chunks, all loads issued before any wait
     // (one round trip); then Q of the first unit and the first chunks' copies
     // (a second round trip, awaited with the first chunk)
-    const int32_t* rec = a.sched + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
+    // the plan's workgroup index: workgroups go to the XCDs in turn
+    // (blockIdx mod 8), so this numbering gives each XCD a contiguous block
+    // of the plan's runs, and a unit's runs mostly share one XCD's L2
+    const int32_t xblk = (a.grid & 7) == 0 ? a.grid >> 3 : 0;
+    const int32_t vb = xblk > 0 ? (int32_t)(blockIdx.x & 7) * xblk + (int32_t)(blockIdx.x >> 3) : (int32_t)blockIdx.x;
+    const int32_t* rec = a.sched + a.s_rec + (int64_t)vb * pakv::kPlanRecord;
     int32_t tab_o[4], tab_l[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {        // B <= 1023: at most four entries per thread
@@ -700,8 +718,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // stream-K runs (per > 0) or unit-aligned runs (per = 0; the unit's
     // workgroups are [rw0, rw1], clamped so that a stale plan stays in bounds)
     const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 0);
-    const int32_t rw0 = clamp_i32(__builtin_amdgcn_readlane(field, 5), 0, (int32_t)blockIdx.x);
-    const int32_t rw1 = clamp_i32(__builtin_amdgcn_readlane(field, 6), (int32_t)blockIdx.x, a.grid - 1);
+    const int32_t rw0 = clamp_i32(__builtin_amdgcn_readlane(field, 5), 0, vb);
+    const int32_t rw1 = clamp_i32(__builtin_amdgcn_readlane(field, 6), vb, a.grid - 1);
     ids = (ids < (uint32_t)a.num_pages) ? ids : 0u;
     __syncthreads();
     if (c_begin >= c_end) return;
@@ -906,19 +924,36 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                             u32x2{cvt_pk_bf16(o[m][0] * inv, o[m][1] * inv), cvt_pk_bf16(o[m][2] * inv, o[m][3] * inv)};
                 }
             } else {
-                const int64_t slot = ((int64_t)blockIdx.x + uc.u) * G;
+                const int64_t slot = ((int64_t)vb + uc.u) * G;
+                // every run of the unit on one XCD (the check needs no
+                // communication: the split and the numbering are fixed)
+                const bool local = xblk > 0 && w0 / xblk == w1 / xblk;
                 mfma_settle();
-                if (col < G) {
-                    float* po = a.part_o + (slot + col) * D + dq;
+                if (local) {
+                    if (col < G) {
+                        float* po = a.part_o + (slot + col) * D + dq;
 #pragma unroll
-                    for (int m = 0; m < C::MT; ++m) put4(po + 16 * m + 4 * qg, o[m]);
-                    if (wave == 0 && qg == 0) put2(a.part_ml + (slot + col) * 2, m_run, l_tot);
-                }
-                // the last of the unit's partials to arrive merges them all
-                if (arrive_last(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket)) {
-                    merge_unit<D>(a, uc, w0, w1, G, threadIdx.x);
-                    if (threadIdx.x == 0)
-                        __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int m = 0; m < C::MT; ++m) put4<true>(po + 16 * m + 4 * qg, o[m]);
+                        if (wave == 0 && qg == 0) put2<true>(a.part_ml + (slot + col) * 2, m_run, l_tot);
+                    }
+                    // the last of the unit's partials to arrive merges them all
+                    if (arrive_last<true>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket)) {
+                        merge_unit<D, true>(a, uc, w0, w1, G, threadIdx.x);
+                        if (threadIdx.x == 0)
+                            __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                } else {
+                    if (col < G) {
+                        float* po = a.part_o + (slot + col) * D + dq;
+#pragma unroll
+                        for (int m = 0; m < C::MT; ++m) put4<false>(po + 16 * m + 4 * qg, o[m]);
+                        if (wave == 0 && qg == 0) put2<false>(a.part_ml + (slot + col) * 2, m_run, l_tot);
+                    }
+                    if (arrive_last<false>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket)) {
+                        merge_unit<D, false>(a, uc, w0, w1, G, threadIdx.x);
+                        if (threadIdx.x == 0)
+                            __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
             }
         }

@@ -44,7 +44,10 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
 //                      the unit-aligned split), grid, B, Hkv, window, max_kv_len
 //   soff [B + 1]       first stream chunk of each sequence's units; soff[B] = T
 //   slen [B]           length of each sequence, clamped to [1, max_kv_len]
-//   rec  [grid][kPlanRecord]  per workgroup: first chunk, end chunk, unit of
+//   rec  [grid][kPlanRecord]  per workgroup w of the plan's numbering (the
+//                      decode kernel's workgroup i takes
+//                      w = (i mod 8) * grid / 8 + i / 8, one block of w per
+//                      XCD, when grid is a multiple of 8): first chunk, end chunk, unit of
 //                      the first chunk, that chunk's index in its unit, chunks
 //                      per workgroup (0 for the unit-aligned split), the first
 //                      and last workgroup of its unit (aligned split only),

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import LayerSpec, bf16_to_f32
+from workloads import LayerSpec, bf16_to_f32, normal_bf16
 
 from gpu_helpers import Scenario, assert_close, dev_bits, host_bits, i32, need_gpu
 
@@ -331,3 +331,34 @@ def test_plan_runs_partition_the_stream(case):
             assert c0 - unit_first[u] == kc and c1 <= unit_first[u] + n[u]       # inside its unit
             assert all(recs[x, 2] == u for x in range(w0, w1 + 1))               # the unit's workgroups
             assert recs[w0, 0] == unit_first[u] and recs[w1, 1] == unit_first[u] + n[u]
+
+
+def test_merges_inside_and_across_xcd_blocks():
+    """Workgroup i runs the plan's workgroup (i mod 8) * 64 + i / 8, so each XCD
+    holds a block of 64 consecutive plan workgroups; a unit whose workgroups lie
+    in one block merges through that XCD's L2, the others through memory.  The
+    E2B full-layer length mix has units of both kinds (checked on the plan);
+    four short sequences added to it give single-workgroup units.  Every output
+    matches the oracle."""
+    need_gpu()
+    from workloads import e2b_decode_workload
+    lens = list(np.array(e2b_decode_workload().cached_lens[:60]) + 1) + [5, 17, 100, 250]
+    spec = LayerSpec("full", 512, 8, 1, 0)
+    sc = Scenario([spec], None, lens, seed=47)
+    sc.store(0, [0] * len(lens), lens)
+    B, maxl = len(lens), max(lens)
+    kv = i32(lens)
+    plan = sc.cache.decode_plan(0, kv, maxl)
+    q = normal_bf16(np.random.default_rng(8), (B, 8, 512))
+    out = host_bits(sc.cache.decode(0, kv, dev_bits(q), maxl, plan=plan))
+    torch.cuda.synchronize()
+    head, recs, _, _ = _read_plan(plan, B, maxl)
+    assert head[2] == 0                                   # the unit-aligned split
+    busy = recs[:, 0] < recs[:, 1]
+    spans = {(int(recs[w, 5]), int(recs[w, 6])) for w in np.nonzero(busy)[0]}
+    inside = [s for s in spans if s[0] < s[1] and s[0] // 64 == s[1] // 64]
+    across = [s for s in spans if s[0] // 64 != s[1] // 64]
+    single = [s for s in spans if s[0] == s[1]]
+    assert inside and across and single, (len(inside), len(across), len(single))
+    ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
+    assert_close(out, ref)
