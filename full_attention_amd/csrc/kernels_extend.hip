@@ -19,10 +19,10 @@
 // never goes through LDS.  V pages are dim-major, so the value MFMA's A operand
 // (one dim, 8 consecutive tokens) is one 16-byte LDS read.
 //
-// Four wavefronts per workgroup, one per SIMD, each owning 512/D blocks of 32
-// rows (D = 512: one, 128 rows per workgroup; D = 256: two, 256 rows, so
-// every K or V operand read from LDS feeds two MFMAs); O^T lives in AGPRs (16
-// tiles), Q^T and the score tiles in VGPRs.  K and V have rings of
+// Four wavefronts per workgroup, each owning 32 rows (128 rows per
+// workgroup); O^T lives in AGPRs (D/32 tiles), Q^T and the score tiles in
+// VGPRs.  At D = 512 a workgroup has its CU (one wavefront per SIMD); at
+// D = 256 two workgroups share a CU.  K and V have rings of
 // two tiles each, and a wavefront's step t runs the score product of tile t+1
 // and the value product of tile t interleaved (two independent MFMA chains),
 // then the softmax of tile t+1; K(t+2) and V(t+1) are copied meanwhile.
@@ -179,7 +179,17 @@ template <int D>
 struct XCfg {
     static constexpr int NW = 4;                        // wavefronts per workgroup, one per SIMD
     static constexpr int THREADS = 64 * NW;
-    static constexpr int NRB = 512 / D;                 // 32-row blocks per wavefront (O^T fills 256 AGPRs)
+    // one 32-row block per wavefront.  At D = 512 its O^T fills the 256
+    // AGPRs and the workgroup has the CU; at D = 256 a wavefront fits in 256
+    // registers, so two workgroups share a CU and one's softmax, prologue and
+    // output overlap the other's matrix work (with two blocks per wavefront
+    // and one workgroup per CU the sliding launch was ~8% slower)
+    static constexpr int NRB = 1;
+    static constexpr int OT = NRB * (D / 32);           // accumulator tiles of O^T
+    static constexpr int MINB = (D == 256) ? 2 : 1;     // workgroups per CU
+    // LDS operands prefetched ahead of the MFMAs; at D = 256 deeper
+    // prefetch spills
+    static constexpr int PF = (D == 256) ? 2 : 4;
     static constexpr int ROWS = 32 * NRB * NW;          // query rows per workgroup
     static constexpr int KROW = D * 2;                  // bytes per K row
     static constexpr int PAGE = 16 * D * 2;             // bytes per (page, head) block
@@ -353,8 +363,8 @@ template <int D, bool HAVE_S, typename Copy, typename Soft, typename SoftEnd>
 __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[8], int v_off,
                                           const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
                                           const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
-                                          f32x16 (&o)[16], int n_copies, Copy copy, Soft soft, SoftEnd soft_end) {
-    constexpr int KK = D / 16, MT = D / 32, PFK = 4, PFV = 4, NRB = XCfg<D>::NRB;
+                                          f32x16 (&o)[XCfg<D>::OT], int n_copies, Copy copy, Soft soft, SoftEnd soft_end) {
+    constexpr int KK = D / 16, MT = D / 32, PFK = XCfg<D>::PF, PFV = XCfg<D>::PF, NRB = XCfg<D>::NRB;
     constexpr int kCopies = kRuns * XCfg<D>::NI;                  // copies per wavefront per step
     constexpr int kCopyGap = (2 * KK) / kCopies;                   // loop steps between copies
     static_assert(kCopyGap >= 1 && (kCopies - 1) * kCopyGap < 2 * KK, "every copy needs a loop step");
@@ -410,7 +420,7 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
 }
 
 template <int D>
-__global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) {
+__global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel(ExtendArgs a) {
     using C = XCfg<D>;
     constexpr int NRB = C::NRB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
@@ -531,10 +541,10 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
     }
     const int v_off = col * 32 + ((h ^ ((col >> 3) & 1)) * 16);
 
-    // O^T tiles: row block rb, output tile m at o[rb * MT + m] (16 tiles)
-    f32x16 o[16];
+    // O^T tiles: row block rb, output tile m at o[rb * MT + m] (OT tiles)
+    f32x16 o[C::OT];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) o[m] = f32x16{};
+    for (int m = 0; m < C::OT; ++m) o[m] = f32x16{};
     float m_run[NRB], l_run[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -542,7 +552,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
         l_run[rb] = 0.f;
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) pin_agpr(o[m]);
+    for (int m = 0; m < C::OT; ++m) pin_agpr(o[m]);
     // the zeros were written by the VALU; the value MFMAs (inline asm, so the
     // compiler does not separate them) read the tiles as SrcC
     asm volatile("s_nop 4" ::: "memory");
@@ -698,7 +708,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS) void extend_kernel(ExtendArgs a) 
             for (int j = 0; j < n_copies; ++j) copy(j);     // a wavefront with no rows still copies its share
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) pin_agpr(o[m]);
+        for (int m = 0; m < C::OT; ++m) pin_agpr(o[m]);
     }
     if (n_tiles > 0) {
         const int32_t t = n_tiles - 1;
