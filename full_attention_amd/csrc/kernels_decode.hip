@@ -249,9 +249,10 @@ __device__ __forceinline__ void build_wg_table(const DecodeArgs& a, const SeqTab
 }
 
 // The schedule of a decode call (the plan): every workgroup of the plan
-// kernel builds the sequence table, takes the run of the chunk stream that
-// decode workgroup blockIdx.x will take and writes its record and the page
-// ids of its chunks; workgroup 0 also writes the header and the table.
+// kernel builds the sequence table, takes run w = blockIdx.x of the chunk
+// stream (the decode workgroup whose plan numbering is w will stream it) and
+// writes its record and the page ids of its chunks; workgroup 0 also writes
+// the header and the table.
 //
 // Runs hold at most per chunks.  When giving every unit its own
 // ceil(n / per) workgroups fits the grid for some per no more than an eighth
