@@ -464,11 +464,13 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
     }
 }
 
-// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
-// other) through device-coherent accesses (the sc1 bit: agent-scope
-// coherence), which need no writeback or invalidation of a whole L2.  They are
-// issued in batches from inline assembly and awaited explicitly; the wait
-// takes the loaded registers as operands, so nothing reads them earlier.
+// Partials cross workgroups, and for a unit spread over XCDs (whose L2s are
+// not coherent with each other) they go through device-coherent accesses (the
+// sc1 bit: agent-scope coherence), which need no writeback or invalidation of
+// a whole L2; a unit on one XCD keeps them in that XCD's L2 (put4 / get4s
+// with LOCAL).  They are issued in batches from inline assembly and awaited
+// explicitly; the wait takes the loaded registers as operands, so nothing
+// reads them earlier.
 //
 // Two hazards the compiler cannot see through this asm are handled by hand:
 // - A store with more than 8 bytes of data reads its data registers after it
