@@ -976,9 +976,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     wait_vm<0>();
 }
 
+// Writes the XCD each workgroup runs on (the hardware XCC id).
+__global__ __launch_bounds__(64) void xcd_probe_kernel(int32_t* out, int32_t n) {
+    uint32_t id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+    if (threadIdx.x == 0 && (int32_t)blockIdx.x < n) out[blockIdx.x] = (int32_t)(id & 0xfu);
+}
+
 }  // namespace
 
 namespace pakv {
+
+int launch_xcd_probe(int32_t* out, int32_t n, void* stream) {
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream), out, n);
+    return (int)hipGetLastError();
+}
 
 static DecodeArgs args_of(const DecodeLaunch& s) {
     DecodeArgs a;

@@ -491,4 +491,12 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
     return hip_status(launch_extend(a, stream), "paged_attn_extend launch");
 }
 
+pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream) {
+    clear_error();
+    if (!out) return fail(PAKV_ERR_INVALID, "null pointer argument");
+    if (num_workgroups < 1 || num_workgroups > 65535)
+        return fail(PAKV_ERR_INVALID, "num_workgroups %d outside [1, 65535]", num_workgroups);
+    return hip_status(launch_xcd_probe(out, num_workgroups, stream), "xcd probe launch");
+}
+
 }  // extern "C"

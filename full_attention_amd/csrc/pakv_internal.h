@@ -122,6 +122,7 @@ struct DecodeLaunch {
 };
 int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
 int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched
+int launch_xcd_probe(int32_t* out, int32_t n, void* stream);  // out[i] = XCD of workgroup i
 
 struct ExtendLaunch {
     SlabView slab;

@@ -32,7 +32,7 @@ EXPORTED = (
     "pakv_paged_kv_store", "pakv_decode_workspace_bytes", "pakv_paged_attn_decode",
     "pakv_decode_plan_bytes", "pakv_decode_plan", "pakv_paged_attn_decode_planned",
     "pakv_paged_attn_decode_append",
-    "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used",
+    "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used", "pakv_workgroup_xcds",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -97,6 +97,8 @@ lib.pakv_set_timing_events.restype = _I
 lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
 lib.pakv_timing_pairs_used.restype = _I
 lib.pakv_timing_pairs_used.argtypes = []
+lib.pakv_workgroup_xcds.restype = _I
+lib.pakv_workgroup_xcds.argtypes = [_P, _I, _P]
 
 
 class PakvError(RuntimeError):
@@ -237,6 +239,11 @@ def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_se
     return _check(lib.pakv_paged_attn_extend(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                              _ptr(prefix_lens), _ptr(q), _ptr(out), num_seqs, total_q,
                                              max_q_len, max_kv_len, _stream(stream)))
+
+
+def workgroup_xcds(out, num_workgroups, stream=None):
+    """out: device int32 [num_workgroups]; out[i] = the XCD workgroup i ran on."""
+    return _check(lib.pakv_workgroup_xcds(_ptr(out), num_workgroups, _stream(stream)))
 
 
 def set_timing_events(events, kernel_mask):

@@ -269,6 +269,16 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
                                    int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                    int32_t max_kv_len, void* stream);
 
+/* Placement check.  Launches num_workgroups (1 .. 65535) workgroups on
+ * stream; workgroup i writes the id of the XCD it ran on to out[i] (device
+ * int32 [num_workgroups], caller-owned).  The decode kernel merges a unit's
+ * partials inside one XCD's L2 when all of the unit's workgroups share a
+ * class of i mod 8, which is correct when workgroups of one class always
+ * share an XCD (the dispatcher hands workgroups to the XCDs in turn); this
+ * call lets a test or a deployment check that on its device.
+ * PAKV_ERR_INVALID for a null out or a count out of range. */
+pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream);
+
 /* Kernel timing hook, for benchmarks and profilers.  events points to 2 *
  * n_pairs hipEvent_t handles (caller-owned, created in the HIP runtime the
  * library runs in); while the hook is set, each store / decode / extend call

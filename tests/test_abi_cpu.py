@@ -262,3 +262,10 @@ def test_one_hip_runtime_per_process():
     maps = open("/proc/self/maps").read()
     runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(runtimes) == 1, runtimes
+
+
+def test_workgroup_xcds_argument_errors_are_returned_before_launch():
+    from full_attention_amd import pakv
+    assert pakv.lib.pakv_workgroup_xcds(None, 8, None) == pakv.ERR_INVALID
+    assert pakv.lib.pakv_workgroup_xcds(0x8000, 0, None) == pakv.ERR_INVALID
+    assert pakv.lib.pakv_workgroup_xcds(0x8000, 65536, None) == pakv.ERR_INVALID

@@ -362,3 +362,21 @@ def test_merges_inside_and_across_xcd_blocks():
     assert inside and across and single, (len(inside), len(across), len(single))
     ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
     assert_close(out, ref)
+
+
+def test_workgroups_of_one_class_mod_8_share_an_xcd():
+    """The decode merge keeps a unit's partials in one XCD's L2 when all of its
+    workgroups lie in one class of i mod 8, which is correct only if those
+    workgroups always run on one XCD (the dispatcher hands workgroups to the
+    XCDs in turn).  Checked over 20 launches of the decode grid's size."""
+    need_gpu()
+    from full_attention_amd import pakv
+    n = 512
+    out = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    for _ in range(20):
+        out.fill_(-1)
+        pakv.workgroup_xcds(out, n)
+        ids = out.cpu().numpy()
+        assert (ids >= 0).all()
+        for c in range(8):
+            assert len(set(ids[c::8].tolist())) == 1, (c, sorted(set(ids[c::8].tolist())))
