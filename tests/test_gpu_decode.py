@@ -380,3 +380,30 @@ def test_workgroups_of_one_class_mod_8_share_an_xcd():
         assert (ids >= 0).all()
         for c in range(8):
             assert len(set(ids[c::8].tolist())) == 1, (c, sorted(set(ids[c::8].tolist())))
+
+
+def test_stream_k_runs_cross_units_and_xcd_blocks():
+    """Many short sequences and one long one: no unit-aligned split fits the
+    grid, so runs are equal pieces of the stream that cross units (a run
+    writes a partial for each unit it touches).  Units merged inside one XCD's
+    block of 64 workgroups and units spread over two blocks both occur (checked
+    on the plan); every output matches the oracle."""
+    need_gpu()
+    lens = [3000] + [40 + (i % 7) for i in range(700)]
+    spec = LayerSpec("full", 256, 8, 1, 0)
+    sc = Scenario([spec], None, lens, seed=53)
+    sc.store(0, [0] * len(lens), lens)
+    B, maxl = len(lens), max(lens)
+    kv = i32(lens)
+    plan = sc.cache.decode_plan(0, kv, maxl)
+    q = normal_bf16(np.random.default_rng(12), (B, 8, 256))
+    out = host_bits(sc.cache.decode(0, kv, dev_bits(q), maxl, plan=plan))
+    torch.cuda.synchronize()
+    head, _, soff, _ = _read_plan(plan, B, maxl)
+    per = int(head[2])
+    assert per > 0                                        # stream-K
+    n = (np.array(lens) + 15) // 16
+    w0, w1 = soff[:B] // per, (soff[:B] + n - 1) // per
+    assert np.any((w0 != w1) & (w0 // 64 == w1 // 64)) and np.any(w0 // 64 != w1 // 64)
+    ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
+    assert_close(out, ref)
