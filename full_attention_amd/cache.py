@@ -80,6 +80,18 @@ class PagedKVCache:
             self._workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._workspace, need
 
+    def status(self):
+        """The decode workspace's status word (pakv.DECODE_* bits), read after
+        the stream's work is done; 0 if no decode ran yet."""
+        if self._workspace is None:
+            return 0
+        torch.cuda.current_stream().synchronize()
+        return int(self._workspace[:4].view(torch.int32).item()) & 0xffffffff
+
+    def clear_status(self):
+        if self._workspace is not None:
+            self._workspace[:4].zero_()
+
     def plan_key(self, layer):
         """Layers with equal keys can share a decode plan (same window and Hkv)."""
         s = self.specs[layer]

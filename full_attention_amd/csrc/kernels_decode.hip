@@ -55,6 +55,11 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 16;        // tokens per staged chunk (one page)
+constexpr uint32_t kNoPage = 0xffffffffu;   // a chunk whose page id lies outside the pool
+// status word bits (sticky: set by a call that detects the condition, cleared
+// only by the caller)
+constexpr uint32_t kStatusPlanMismatch = 1u;    // the plan was made for another shape
+constexpr uint32_t kStatusXcdSplit = 2u;        // an XCD-local unit's workgroups ran on several XCDs
 
 struct DecodeArgs {
     const uint8_t* k_slab;
@@ -75,6 +80,7 @@ struct DecodeArgs {
     int32_t grid;           // workgroups
     int32_t* sched;         // schedule buffer (word offsets below)
     int64_t s_soff, s_slen, s_rec, s_ids, s_cap;
+    uint32_t* status;       // sticky status word (kStatus* bits), read by the caller
     uint32_t* arrivals;     // [U] partials written per unit; zero between calls
     float* part_o;          // [grid + U][G][D]
     float* part_ml;         // [grid + U][G][2]
@@ -205,8 +211,9 @@ __device__ __forceinline__ void build_seq_table(const DecodeArgs& a, const int32
 }
 
 // Page id of stream chunk c: the page of sequence b holding the chunk's 16
-// keys.  Ids outside the pool become 0, so a bad table never makes a copy
-// leave the slab.
+// keys.  Ids outside the pool become kNoPage: the decode kernel reads page 0
+// in their place (so a bad table never makes a copy leave the slab) and an
+// append never writes to them.
 __device__ __forceinline__ uint32_t page_of_chunk(const DecodeArgs& a, const int32_t* __restrict__ page_table,
                                                   const SeqTable& st, int32_t B, int32_t c) {
     const int32_t b = seq_of_chunk(st, B, c);
@@ -214,7 +221,7 @@ __device__ __forceinline__ uint32_t page_of_chunk(const DecodeArgs& a, const int
     const int32_t n = chunks_of(a, len);
     const int32_t k = (c - st.soff[b]) % n;
     const int32_t ph = page_table[(int64_t)b * a.max_pages + (window_lo(a, len) >> 4) + k];
-    return ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : 0u;
+    return ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : kNoPage;
 }
 
 // Prefix over sequences of the decode workgroups an aligned split gives them
@@ -343,18 +350,22 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
     }
     for (int32_t j = t; j < max(c_end - c_begin, 64); j += 256) {
         const bool in_run = c_begin + j < c_end;
-        const uint32_t id = in_run ? page_of_chunk(a, page_table, st, B, c_begin + j) : 0u;
+        const uint32_t id = in_run ? page_of_chunk(a, page_table, st, B, c_begin + j) : kNoPage;
         if (j < 64) rec[pakv::kPlanRecIds + j] = (int32_t)id;
         if (in_run) S[a.s_ids + c_begin + j] = (int32_t)id;
     }
 }
 
 // Page ids of stream chunks c0 .. c0 + count - 1 from the schedule (lane j
-// holds chunk c0 + j; lanes past `count` hold 0), re-clamped to the pool.
+// holds chunk c0 + j; lanes past `count` hold kNoPage), as the plan wrote
+// them: the copies clamp them to the pool (issue_chunk).
+// (The lane index is made opaque here so that the address is formed where it
+// is used, once per 64 chunks, instead of being held in registers all along.)
 __device__ __forceinline__ uint32_t sched_ids(const DecodeArgs& a, int32_t c0, int32_t count, int lane) {
-    uint32_t id = 0;
+    asm volatile("" : "+v"(lane));
+    uint32_t id = kNoPage;
     if (lane < count && c0 + lane < a.s_cap) id = (uint32_t)a.sched[a.s_ids + c0 + lane];
-    return (id < (uint32_t)a.num_pages) ? id : 0u;
+    return id;
 }
 
 // Q^T operand of a wave's dim quarter: column `col` = head g*G + col (zero
@@ -394,9 +405,12 @@ __device__ __forceinline__ void take_q(u32x4 (&qreg)[N], bool real) {
 // waits for a chunk's K and for its V still cover everything (they can only
 // wait for one copy more than needed).
 template <int D, bool INT8>
-__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, uint8_t* buf, const Unit& x,
+__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, uint32_t raw_id, uint8_t* buf, const Unit& x,
                                             bool last, uint8_t* stage, int32_t* newp, int wave, int lane) {
     using C = Cfg<D, INT8>;
+    // an id outside the pool (a missing page or a stale plan) reads page 0
+    const bool in_pool = raw_id < (uint32_t)a.num_pages;
+    const int32_t phys = in_pool ? (int32_t)raw_id : 0;
     const int64_t blk = ((int64_t)phys * a.hkv + x.g) * C::PAGE;
     const uint8_t* kp = a.k_slab + blk;       // wave-uniform bases; per-lane 32-bit offsets
     const uint8_t* vp = a.v_slab + blk;
@@ -407,7 +421,7 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int32_t phys, u
             const int r = (x.hi - 1) & 15;                              // slot of position L - 1
             if (wave == 0) {
                 if (lane < D / 8) dma16_s(a.v_new + nrow, (uint32_t)(lane * 16), lds_addr_of(stage));
-                if (lane == 0) *newp = phys;
+                if (lane == 0) *newp = in_pool ? phys : -1;   // -1: the new row has no page to go to
             }
 #pragma unroll
             for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
@@ -521,19 +535,35 @@ __device__ __forceinline__ void await(T (&regs)[N]) {
 }
 
 // Counts this workgroup's arrival at a unit and reports whether it was the
-// last of `expected` (then every partial of the unit is complete).
+// last of `expected` (then every partial of the unit is complete).  The
+// counter's low 16 bits count arrivals.  On the XCD-local path each workgroup
+// first sets bit 16 + (its XCD) in the same word, and the last to arrive
+// checks that one bit is set in all: a unit whose workgroups ran on several
+// XCDs exchanged its partials through L2s that do not see each other, so the
+// merge may have read stale data, and the status word records it.  (The two
+// atomics of one thread go to one address in order: the first is complete,
+// vmcnt(0), before the second issues.)
 template <bool LOCAL>
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* ticket) {
-    wait_vm<0>();               // this wave's partial stores are complete
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* ticket, uint32_t xcc,
+                                            uint32_t* status) {
+    if (LOCAL && threadIdx.x == 0) {
+        asm volatile("" : "+s"(xcc));   // form the flag here, not early in the kernel
+        __hip_atomic_fetch_or(counter, 1u << (16 + xcc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vm<0>();               // this wave's partial stores (and the flag) are complete
     lds_barrier();              // ... and every wave's
     if (threadIdx.x == 0) {
+        uint32_t old;
         if constexpr (LOCAL)
-            *ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         else
-            *ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *ticket = old;
+        if (LOCAL && (old & 0xffffu) == expected - 1 && (old >> 16) != (1u << xcc))
+            __hip_atomic_fetch_or(status, kStatusXcdSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     lds_barrier();
-    return *ticket == expected - 1;
+    return (*ticket & 0xffffu) == expected - 1;
 }
 
 // One batch of a unit's merge: partial slots sl0, sl0 + G, ... (CNT of them,
@@ -590,7 +620,7 @@ __device__ __forceinline__ void merge_batch(const float* o_base, const float* ml
 // workgroup's own bandwidth bounds the merge, so the batches carry no
 // padding.
 template <int D, bool LOCAL>
-__device__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Unit& x, int32_t w0, int32_t w1, int32_t G, int t) {
     constexpr int IPT = D / 128;
     constexpr int TPH = (D / 4) / IPT;                 // threads per head (32)
     constexpr int BATCH = (D == 512) ? 7 : 8;
@@ -688,6 +718,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int32_t G = a.group;
     const int32_t B = a.num_seqs;
     const int32_t U = B * a.hkv;
+    uint32_t xcc;                        // the XCD this workgroup runs on
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= 15u;
 
     // the schedule: the sequence table into LDS, this workgroup's record and
     // the page ids of its first 64 chunks, all loads issued before any wait
@@ -707,6 +740,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         tab_l[k] = (i < B) ? a.sched[a.s_slen + i] : 1;
     }
     const int32_t field = rec[min(lane, 7)];
+    const int32_t hdr = a.sched[min(lane, 7)];     // the plan's header
     uint32_t ids = (uint32_t)rec[pakv::kPlanRecIds + lane];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -723,8 +757,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 0);
     const int32_t rw0 = clamp_i32(__builtin_amdgcn_readlane(field, 5), 0, vb);
     const int32_t rw1 = clamp_i32(__builtin_amdgcn_readlane(field, 6), vb, a.grid - 1);
-    ids = (ids < (uint32_t)a.num_pages) ? ids : 0u;
     __syncthreads();
+    // a plan made for another shape (sequences, Hkv, window, length bound or
+    // grid) describes another split: every workgroup returns before touching
+    // a counter or an output, and the status word says why
+    {
+        const bool same = __builtin_amdgcn_readlane(hdr, 0) == pakv::kPlanMagic &&
+                          __builtin_amdgcn_readlane(hdr, 3) == a.grid && __builtin_amdgcn_readlane(hdr, 4) == B &&
+                          __builtin_amdgcn_readlane(hdr, 5) == a.hkv && __builtin_amdgcn_readlane(hdr, 6) == a.window &&
+                          __builtin_amdgcn_readlane(hdr, 7) == a.max_kv_len;
+        if (!same) {
+            if (blockIdx.x == 0 && threadIdx.x == 0)
+                __hip_atomic_fetch_or(a.status, kStatusPlanMismatch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
     if (c_begin >= c_end) return;
     const int32_t total = c_end - c_begin;
 
@@ -738,7 +785,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
-            issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui,
+            issue_chunk<D, INT8>(a, (uint32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui,
                                  ki == ui.n - 1, stage + c * C::STAGE, newp + c, wave, lane);
             advance(a, st, U, ui, ki);
         }
@@ -772,7 +819,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                     ids = sched_ids(a, c_begin + j, min(total - j, 64), lane);
                     wait_vm<0>();
                 }
-                issue_chunk<D, INT8>(a, (int32_t)__builtin_amdgcn_readlane(ids, j & 63),
+                issue_chunk<D, INT8>(a, (uint32_t)__builtin_amdgcn_readlane(ids, j & 63),
                                      lds + (j % C::NBUF) * C::BUF, ui, ki == ui.n - 1,
                                      stage + (j % C::NBUF) * C::STAGE, newp + (j % C::NBUF), wave, lane);
                 advance(a, st, U, ui, ki);
@@ -787,17 +834,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                 // in LDS, from k_new) and its staged V values to the slab; the V
                 // values are patched into the staged page once its copies have
                 // landed (after the score exchange)
+                // (a position whose page id lies outside the pool is not
+                // written, as the store drops such rows; it is still attended)
                 const int r = (uc.hi - 1) & 15;
                 const uint8_t* sg = stage + (i % C::NBUF) * C::STAGE;
-                const int64_t blk = ((int64_t)newp[i % C::NBUF] * a.hkv + uc.g) * C::PAGE;
-                uint8_t* kdst = const_cast<uint8_t*>(a.k_slab) + blk + r * C::ROW;
-                uint8_t* vdst = const_cast<uint8_t*>(a.v_slab) + blk + r * 2;
-                for (int d = threadIdx.x; d < D; d += 256)
-                    *reinterpret_cast<uint16_t*>(vdst + d * 32) = *reinterpret_cast<const uint16_t*>(sg + 2 * d);
-                if (threadIdx.x < C::ROW / 16) {
-                    const int c = threadIdx.x;
-                    *reinterpret_cast<u32x4*>(kdst + c * 16) =
-                        *reinterpret_cast<const u32x4*>(kbuf + r * C::ROW + ((c ^ (r & 15)) * 16));
+                const int32_t np = newp[i % C::NBUF];
+                if (np >= 0) {
+                    const int64_t blk = ((int64_t)np * a.hkv + uc.g) * C::PAGE;
+                    uint8_t* kdst = const_cast<uint8_t*>(a.k_slab) + blk + r * C::ROW;
+                    uint8_t* vdst = const_cast<uint8_t*>(a.v_slab) + blk + r * 2;
+                    for (int d = threadIdx.x; d < D; d += 256)
+                        *reinterpret_cast<uint16_t*>(vdst + d * 32) = *reinterpret_cast<const uint16_t*>(sg + 2 * d);
+                    if (threadIdx.x < C::ROW / 16) {
+                        const int c = threadIdx.x;
+                        *reinterpret_cast<u32x4*>(kdst + c * 16) =
+                            *reinterpret_cast<const u32x4*>(kbuf + r * C::ROW + ((c ^ (r & 15)) * 16));
+                    }
                 }
             }
         }
@@ -940,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                         if (wave == 0 && qg == 0) put2<true>(a.part_ml + (slot + col) * 2, m_run, l_tot);
                     }
                     // the last of the unit's partials to arrive merges them all
-                    if (arrive_last<true>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket)) {
+                    if (arrive_last<true>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status)) {
                         merge_unit<D, true>(a, uc, w0, w1, G, threadIdx.x);
                         if (threadIdx.x == 0)
                             __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -952,7 +1004,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                         for (int m = 0; m < C::MT; ++m) put4<false>(po + 16 * m + 4 * qg, o[m]);
                         if (wave == 0 && qg == 0) put2<false>(a.part_ml + (slot + col) * 2, m_run, l_tot);
                     }
-                    if (arrive_last<false>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket)) {
+                    if (arrive_last<false>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status)) {
                         merge_unit<D, false>(a, uc, w0, w1, G, threadIdx.x);
                         if (threadIdx.x == 0)
                             __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1016,6 +1068,7 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.s_rec = s.layout.rec;
     a.s_ids = s.layout.ids;
     a.s_cap = s.layout.cap;
+    a.status = s.status;
     a.arrivals = s.arrivals;
     a.part_o = s.part_o;
     a.part_ml = s.part_ml;

@@ -49,16 +49,17 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs) {
     return p;
 }
 
-// Workspace: arrival counters (a fixed region of kDecodeMaxUnits, so that
-// layers of any shape can share one workspace and leave it zeroed), then
-// partial o, then partial (m, l); 256-byte aligned parts.
+// Workspace: the status word's block, arrival counters (a fixed region of
+// kDecodeMaxUnits, so that layers of any shape can share one workspace and
+// leave it zeroed), then partial o, then partial (m, l); 256-byte aligned
+// parts.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_partial_bytes(const pakv_layer_desc& d, int32_t num_seqs) {
     DecodePlan p = plan_decode(d, num_seqs);
     size_t slots = (size_t)(p.grid + p.units) * p.group;
-    return align256((size_t)kDecodeMaxUnits * sizeof(uint32_t)) + align256(slots * d.head_dim * sizeof(float)) +
-           align256(slots * 2 * sizeof(float));
+    return kDecodeStatusBytes + align256((size_t)kDecodeMaxUnits * sizeof(uint32_t)) +
+           align256(slots * d.head_dim * sizeof(float)) + align256(slots * 2 * sizeof(float));
 }
 
 PlanLayout plan_layout(int32_t num_seqs, int32_t hkv, int32_t max_kv_len) {
@@ -332,12 +333,15 @@ static pakv_status decode_setup(const pakv_layer_map* map, int32_t layer, const 
     return PAKV_OK;
 }
 
-// Workspace: arrival counters (a fixed region of kDecodeMaxUnits, so that
-// layers of any shape can share one workspace and leave it zeroed), partial o,
-// partial (m, l); then, for the unplanned call, its schedule.
+// Workspace: the status word (in a block of kDecodeStatusBytes), arrival
+// counters (a fixed region of kDecodeMaxUnits, so that layers of any shape
+// can share one workspace and leave it zeroed), partial o, partial (m, l);
+// then, for the unplanned call, its schedule.
 static void bind_partials(DecodeLaunch& a, void* workspace) {
     size_t slots = (size_t)(a.plan.grid + a.plan.units) * a.plan.group;
     char* ws = static_cast<char*>(workspace);
+    a.status = reinterpret_cast<uint32_t*>(ws);
+    ws += kDecodeStatusBytes;
     a.arrivals = reinterpret_cast<uint32_t*>(ws);
     ws += align256((size_t)kDecodeMaxUnits * sizeof(uint32_t));
     a.part_o = reinterpret_cast<float*>(ws);

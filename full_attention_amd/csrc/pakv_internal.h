@@ -29,6 +29,7 @@ void clear_error();
 constexpr int32_t kDecodeGrid = 512;
 constexpr int32_t kDecodeMaxSeqs = 1023;     // sequences per decode call
 constexpr int32_t kDecodeMaxUnits = 8192;    // num_seqs * Hkv per decode call
+constexpr size_t kDecodeStatusBytes = 256;   // the workspace's first block: the status word
 struct DecodePlan {
     int32_t grid;           // workgroups of pass 1
     int32_t units;          // num_seqs * Hkv
@@ -52,9 +53,9 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
 //                      per workgroup (0 for the unit-aligned split), the first
 //                      and last workgroup of its unit (aligned split only),
 //                      spare words, then from word kPlanRecIds the page ids of
-//                      its first 64 chunks (0 past its run)
+//                      its first 64 chunks (-1 past its run)
 //   ids  [cap]         page id of every stream chunk (ids outside the pool
-//                      already replaced by 0)
+//                      replaced by -1: read as page 0, never written)
 constexpr int32_t kPlanMagic = 0x31504b50;
 constexpr int32_t kPlanHeader = 16;
 constexpr int32_t kPlanRecord = 80;
@@ -113,6 +114,7 @@ struct DecodeLaunch {
     DecodePlan plan;
     int32_t* sched;     // the schedule buffer (written by the plan kernel, read by the decode kernel)
     PlanLayout layout;
+    uint32_t* status;   // sticky status word (workspace offset 0)
     uint32_t* arrivals; // [units], zero between calls
     float* part_o;      // [grid + units][G][D]
     float* part_ml;     // [grid + units][G][2]

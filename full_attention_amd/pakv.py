@@ -36,6 +36,7 @@ EXPORTED = (
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
+DECODE_PLAN_MISMATCH, DECODE_XCD_SPLIT = 1, 2     # bits of the decode workspace's status word
 
 
 class LayerDesc(ctypes.Structure):

@@ -182,6 +182,8 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
  * pakv_paged_attn_decode_planned as well). */
 size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
                                    int32_t num_seqs, int32_t max_kv_len);
+#define PAKV_DECODE_PLAN_MISMATCH 1u
+#define PAKV_DECODE_XCD_SPLIT 2u
 
 /* One decode query per sequence.
  *   kv_lens     : device int32 [num_seqs], tokens stored for the sequence
@@ -192,8 +194,18 @@ size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
  *   max_kv_len  : host upper bound on kv_lens (lengths above it are clamped)
  *   workspace   : device memory of at least pakv_decode_workspace_bytes(...),
  *                 zero-filled before its first use; every call leaves it
- *                 zero-filled again (per-sequence arrival counters live there).
+ *                 zero-filled again (per-sequence arrival counters live there),
+ *                 except for its first 32-bit word, the status word below.
  *                 Calls that may overlap need separate workspaces.
+ * Status word (workspace bytes 0..3): bits that a call sets when its kernel
+ * detects a condition it cannot report through the return value (the kernel
+ * runs after the call returns); they stay set until the caller clears them.
+ *   PAKV_DECODE_PLAN_MISMATCH : the plan given to a planned or append call was
+ *                 made for another num_seqs, Hkv, window or max_kv_len; the
+ *                 call then wrote no output and changed nothing else.
+ *   PAKV_DECODE_XCD_SPLIT     : some unit merged inside one XCD's L2 had
+ *                 workgroups on several XCDs (see pakv_workgroup_xcds); its
+ *                 outputs may be wrong.
  * num_seqs must not exceed 1023 and num_seqs * Hkv 8192 (PAKV_ERR_UNSUPPORTED).
  * A shared layer reads its source's slab (and scales) with its own descriptor
  * (window, sm_scale, Hq).  The keys of all sequences form one stream of
@@ -215,9 +227,12 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
  * stream) and pakv_paged_attn_decode_planned runs a layer's attention from it.
  * A plan made for `layer` serves every layer with the same window and Hkv
  * while kv_lens, the page table, num_seqs and max_kv_len stay as they were
- * when it was made; the caller keeps to that (the kernel cannot tell, but
- * re-clamps page ids to the slab, so a stale plan gives wrong values, never a
- * read outside the slab).  The planned call takes the same arguments and
+ * when it was made.  The kernel checks the plan's header against the call's
+ * num_seqs, Hkv, window and max_kv_len: on a mismatch it writes nothing and
+ * sets PAKV_DECODE_PLAN_MISMATCH in the workspace's status word.  Changed
+ * kv_lens or page table entries under an unchanged header it cannot tell:
+ * page ids are re-clamped to the slab, so such a stale plan gives wrong
+ * values, never an access outside the slab.  The planned call takes the same arguments and
  * workspace as pakv_paged_attn_decode, minus kv_lens, and gives bit-identical
  * output. */
 size_t pakv_decode_plan_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_kv_len);
@@ -242,7 +257,9 @@ pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t la
  *   k_new, v_new : device bf16 [num_seqs][Hkv][D], owned by the caller
  *   plan         : from pakv_decode_plan for this step (it carries kv_lens)
  * Other arguments as in pakv_paged_attn_decode_planned; kv_lens[b] must not
- * exceed max_kv_len.  A shared layer stores nothing (its source's call stored
+ * exceed max_kv_len.  A row whose page id (page_table[b][(kv_lens[b]-1)/16])
+ * lies outside [0, num_pages) is not written, as pakv_paged_kv_store drops
+ * such rows; the new token is still attended.  A shared layer stores nothing (its source's call stored
  * the row) and k_new/v_new may be NULL: the call is then a planned decode.  An
  * owning layer with int8 K/V returns PAKV_ERR_UNSUPPORTED before any launch
  * (call pakv_paged_kv_store, then the planned decode). */

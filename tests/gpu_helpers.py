@@ -36,8 +36,19 @@ def i32(x):
     return torch.tensor(np.asarray(x, dtype=np.int32), dtype=torch.int32).cuda()
 
 
-def assert_close(gpu_bits, ref, what=""):
-    """Elementwise |gpu - ref| <= ATOL + RTOL * |ref| (bf16 outputs vs float64)."""
+def error_stats(gpu_bits, ref):
+    """(max abs err, RMS(err) / RMS(ref)) of bf16 outputs against float64."""
+    got = bf16_to_f32(gpu_bits).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = got - ref
+    rms_ref = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    rel = float(np.sqrt(np.mean(err * err)) / rms_ref) if rms_ref > 0 else float("nan")
+    return float(np.abs(err).max()) if err.size else 0.0, rel
+
+
+def assert_close(gpu_bits, ref, what="", report=False):
+    """Elementwise |gpu - ref| <= ATOL + RTOL * |ref| (bf16 outputs vs float64).
+    report: print the max abs error and RMS(err) / RMS(ref)."""
     got = bf16_to_f32(gpu_bits).astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -46,6 +57,10 @@ def assert_close(gpu_bits, ref, what=""):
     bad = err > ATOL + RTOL * np.abs(ref)
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; "
                            f"max abs err {err.max():.3e}")
+    if report:
+        mx, rel = error_stats(gpu_bits, ref)
+        print(f"[parity] {what}: max abs err {mx:.3e}, RMS(err)/RMS(ref) {rel:.3e}, "
+              f"RMS(ref) {np.sqrt(np.mean(ref * ref)):.3e}", flush=True)
     return float(err.max())
 
 
@@ -98,6 +113,15 @@ class Scenario:
         self.rows[layer] = (k, v, cu, list(starts))
         return k, v
 
+    def store_rows(self, layer, starts, counts, k, v):
+        """Stores given rows (uint16 bf16 bits [T, Hkv, D]) on both sides."""
+        cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        self.cache.store(layer, i32(cu), i32(starts), dev_bits(k), dev_bits(v))
+        for b in range(self.B):
+            if counts[b]:
+                self.oracle.store(layer, b, int(starts[b]), k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]])
+        self.rows[layer] = (k, v, cu, list(starts))
+
     def decode(self, layer, kv_lens, seqs=None):
         s = self.specs[layer]
         q = normal_bf16(self.rng, (self.B, s.num_q_heads, s.head_dim))
@@ -108,10 +132,11 @@ class Scenario:
         ref = np.stack([self.oracle.decode(layer, b, q[b], int(kv_lens[b])) for b in seqs])
         return got[list(seqs)], ref, q
 
-    def extend(self, layer, prefixes, chunks, seqs=None):
+    def extend(self, layer, prefixes, chunks, seqs=None, q=None):
         s = self.specs[layer]
         total = int(sum(chunks))
-        q = normal_bf16(self.rng, (max(total, 1), s.num_q_heads, s.head_dim))[:total]
+        if q is None:
+            q = normal_bf16(self.rng, (max(total, 1), s.num_q_heads, s.head_dim))[:total]
         cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
         max_kv = int(max(p + n for p, n in zip(prefixes, chunks)))
         out = self.cache.extend(layer, i32(cu), i32(prefixes), dev_bits(q), int(max(chunks)), max_kv)

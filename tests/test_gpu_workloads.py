@@ -39,13 +39,22 @@ class DeviceScenario:
         self.sample = list(sample)
         self.kept = {}      # (owner layer, seq) -> (positions, k f32, v f32) on the host
 
-    def store(self, layer, starts, counts):
+    def store(self, layer, starts, counts, make_rows=None):
+        """make_rows(layer, positions [T] int64 device tensor, k) -> (k, v) device
+        bf16 bits, to replace the N(0, 1) draws (v may be None: drawn)."""
         if self.cache.sources[layer] != layer:
             return
         s = self.wl.layers[layer]
         cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
         k = self.draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
-        v = self.draws.rms_normalised(k) if s.k_eq_v else self.draws.bf16((int(cu[-1]), s.num_kv_heads, s.head_dim))
+        v = None
+        if make_rows is not None:
+            pos = torch.cat([torch.arange(st, st + c, device="cuda", dtype=torch.int64)
+                             for st, c in zip(starts, counts)])
+            k, v = make_rows(layer, pos, k)
+        if v is None:
+            v = self.draws.rms_normalised(k) if s.k_eq_v else self.draws.bf16((int(cu[-1]), s.num_kv_heads,
+                                                                               s.head_dim))
         self.cache.store(layer, i32(cu), i32(starts), k, v)
         for b in self.sample:
             if counts[b] == 0:
@@ -72,11 +81,20 @@ class DeviceScenario:
         return pos, k.astype(np.float64), v.astype(np.float64)
 
 
+def _sample(lens, n_sample):
+    """The longest sequence always, then the shortest, then the median one."""
+    order = np.argsort(lens, kind="stable")
+    picks = []
+    for i in (int(order[-1]), int(order[0]), int(order[len(order) // 2])):
+        if i not in picks:
+            picks.append(i)
+    return sorted(picks[:n_sample])
+
+
 def _decode_workload(wl, n_sample=3, layers=None):
     lens = np.array(wl.cached_lens, dtype=np.int64)
     kv = lens + 1
-    order = np.argsort(lens)
-    sample = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})[:n_sample]
+    sample = _sample(lens, n_sample)
     sc = DeviceScenario(wl, kv, sample)
     for l, s in enumerate(wl.layers):
         lo = np.maximum(0, kv - s.window) if s.window else np.zeros_like(kv)
@@ -97,7 +115,8 @@ def _decode_workload(wl, n_sample=3, layers=None):
         for b in sample:
             pos, k, v = sc.rows(l, b)
             ref = attend(qf[b:b + 1], np.array([kv[b] - 1]), k, v, pos, s.window, s.sm_scale)[0]
-            worst = max(worst, assert_close(got[b], ref, f"{wl.name} layer {l} seq {b}"))
+            worst = max(worst, assert_close(got[b], ref, f"{wl.name} layer {l} seq {b} (L {kv[b]})",
+                                            report=(l < 2)))
     return worst
 
 
@@ -168,4 +187,130 @@ def test_e2b_extend_full_size():
         for b in range(len(P)):
             pos, k, v = sc.rows(l, b)
             ref = attend(qf[cu[b] + rows], P[b] + rows, k, v, pos, s.window, s.sm_scale)
-            assert_close(out[cu[b] + rows], ref, f"E2B extend layer {l} seq {b}")
+            assert_close(out[cu[b] + rows], ref, f"E2B extend layer {l} seq {b}", report=(l in (0, 4)))
+
+
+# ---- closed forms at full size ------------------------------------------------
+# With q = 0 every visible key scores 0, so the output is the plain mean of the
+# visible value rows, whatever the keys hold.  Value row j carries A = D in one
+# dimension, (j // s) mod D with s = n_visible // D, and 0 elsewhere, so every
+# dimension of the output is A * (its keys) / n_visible, about 1; a page (16
+# keys) dropped, counted twice or taken from the wrong place moves some
+# dimension by at least A * 16 / n_visible (0.06 at 131,073 keys), past the
+# tolerance.  Every page of every split of the stream counts.
+
+def _bucket_rows(wl, lens_visible):
+    """make_rows for DeviceScenario.store: one-hot value rows by position."""
+    def make(layer, pos, k):
+        s = wl.layers[layer]
+        d = s.head_dim
+        step = max(1, int(lens_visible[layer]) // d)
+        v = torch.zeros((pos.numel(), s.num_kv_heads, d), dtype=torch.bfloat16, device="cuda")
+        dim = (pos // step) % d
+        v[torch.arange(pos.numel(), device="cuda"), :, dim] = float(d)
+        return k, v.view(torch.int16)
+    return make
+
+
+def _closed_form_mean(window, kv_len, d, lens_visible):
+    lo = max(0, kv_len - window) if window else 0
+    step = max(1, int(lens_visible) // d)
+    dims = (np.arange(lo, kv_len) // step) % d
+    return np.bincount(dims, minlength=d).astype(np.float64) * d / (kv_len - lo)
+
+
+def _check_bucket_decode(wl, sample, seqs_label):
+    lens = np.array(wl.cached_lens, dtype=np.int64)
+    kv = lens + 1
+    n_vis = {l: (min(int(kv.max()), s.window) if s.window else int(kv.max())) for l, s in enumerate(wl.layers)}
+    sc = DeviceScenario(wl, kv, sample)
+    for l, s in enumerate(wl.layers):
+        lo = np.maximum(0, kv - s.window) if s.window else np.zeros_like(kv)
+        sc.store(l, lo, kv - lo, make_rows=_bucket_rows(wl, n_vis))
+    for l, s in enumerate(wl.layers):
+        if sc.cache.sources[l] != l:
+            continue
+        q = torch.zeros((sc.B, s.num_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+        got = host_bits(sc.cache.decode(l, i32(kv), q, int(kv.max())))
+        torch.cuda.synchronize()
+        for b in sample:
+            pos, k, v = sc.rows(l, b)
+            ref = attend(np.zeros((1, s.num_q_heads, s.head_dim)), np.array([kv[b] - 1]), k, v, pos, s.window,
+                         s.sm_scale)[0]
+            closed = _closed_form_mean(s.window, int(kv[b]), s.head_dim, n_vis[l])
+            # the oracle agrees with the closed form (int8: to the encoding's error)
+            tol = 1e-3 if s.kv_dtype == "int8" else 1e-9
+            assert np.abs(ref - closed[None, :]).max() < tol
+            assert_close(got[b], ref, f"{wl.name} {seqs_label} layer {l} seq {b}: q = 0, one-hot values", report=True)
+
+
+def test_int8_long_context_every_page_counts():
+    """131,073 keys per sequence, all 8 sequences, both int8 layers."""
+    need_gpu()
+    _check_bucket_decode(int8_long_workload(), list(range(8)), "all sequences")
+
+
+def test_moe26b_longest_sequence_every_page_counts():
+    """The 26B-like stack's sliding layers (V free), on its longest sequence."""
+    need_gpu()
+    wl = moe26b_decode_workload()
+    keep = [l for l, s in enumerate(wl.layers) if not s.k_eq_v]
+    import copy
+    sub = copy.copy(wl)
+    sub.layers = [wl.layers[l] for l in keep[:3]]
+    _check_bucket_decode(sub, _sample(np.array(wl.cached_lens), 1), "longest sequence")
+
+
+def test_moe26b_longest_sequence_planted_keys():
+    """The 26B-like full layers (V = RMS-normalised K) on their full stack:
+    keys planted every 1,000 positions (first page, page edges, the last
+    position) point along their own dimension d_m with length 544, and every
+    query is the sum of those directions, so each planted key scores about 24
+    and all other keys about 0 +- 0.2: the output is the mean of the planted
+    keys' value rows (sqrt(D) along d_m), about 1.4 in each d_m; a split that
+    is dropped or merged twice moves some d_m by 0.1 or more."""
+    need_gpu()
+    wl = moe26b_decode_workload()
+    lens = np.array(wl.cached_lens, dtype=np.int64)
+    kv = lens + 1
+    longest = _sample(lens, 1)
+    marks = sorted(set([0, 15, 16] + list(range(1000, int(kv.max()), 1000)) + [int(kv[longest[0]]) - 1]))
+    marks_t = torch.tensor(marks, device="cuda", dtype=torch.int64)
+
+    def dims_of(n, d):
+        return [(7 + 29 * m) % d for m in range(n)]
+
+    def make(layer, pos, k):
+        s = wl.layers[layer]
+        if not s.k_eq_v:
+            return k, None
+        hit = torch.isin(pos, marks_t)
+        idx = torch.nonzero(hit).flatten()
+        m = torch.searchsorted(marks_t, pos[idx])
+        dims = torch.tensor(dims_of(len(marks), s.head_dim), device="cuda")[m]
+        kb = k.view(torch.bfloat16)
+        kb[idx] = 0
+        kb[idx, :, dims] = 544.0
+        return kb.view(torch.int16), None
+
+    sc = DeviceScenario(wl, kv, longest)
+    full = [l for l, s in enumerate(wl.layers) if s.k_eq_v]
+    for l in full:
+        sc.store(l, np.zeros_like(kv), kv, make_rows=make)
+    b = longest[0]
+    for l in full:
+        s = wl.layers[l]
+        qv = np.zeros((sc.B, s.num_q_heads, s.head_dim), dtype=np.float32)
+        for m, dm in enumerate(dims_of(len(marks), s.head_dim)):
+            if marks[m] < kv[b]:
+                qv[:, :, dm] = 1.0
+        from workloads import bf16_from_f32
+        qb = bf16_from_f32(qv)
+        q = torch.from_numpy(qb.view(np.int16)).cuda()
+        got = host_bits(sc.cache.decode(l, i32(kv), q, int(kv.max())))
+        torch.cuda.synchronize()
+        pos, k, v = sc.rows(l, b)
+        ref = attend(bf16_to_f32(qb[b:b + 1]).astype(np.float64), np.array([kv[b] - 1]), k, v, pos, 0,
+                     s.sm_scale)[0]
+        assert ref.max() > 1.0                       # the planted keys carry the output
+        assert_close(got[b], ref, f"26B full layer {l} seq {b} (L {kv[b]}): planted keys", report=True)

@@ -90,3 +90,69 @@ def test_positions_past_kv_len_are_ignored():
     pos, k, v = c2.values(1, 0)
     want = attend(bf16_bits_to_f32(q)[None], np.array([19]), k[:20], v[:20], pos[:20], 0, 0.25)[0]
     assert np.array_equal(a, want)
+
+
+# ---- extend positions and the key cut (hand-worked) -------------------------
+# An extend chunk of n queries after a cached prefix of P tokens sits at
+# positions P .. P + n - 1 (FreeToken PR #898, description, fourth bullet: the
+# chunk follows what the cache already holds); the tiny workload's chunk after
+# its decode token starts at 101 and ends at 164.
+
+from oracle import extend_positions
+
+
+def test_extend_positions_hand_typed():
+    assert extend_positions(3, 2).tolist() == [3, 4]
+    assert extend_positions(0, 1).tolist() == [0]
+    assert extend_positions(5, 0).tolist() == []
+    pos = extend_positions(101, 64)
+    assert pos[0] == 101 and pos[-1] == 164 and len(pos) == 64
+
+
+def _scalar_layers(window):
+    # D = 1, one head; sm_scale irrelevant once q = 0
+    return [dict(type="sliding" if window else "full", head_dim=1, num_q_heads=1, num_kv_heads=1,
+                 window=window, kv_dtype="bf16", sm_scale=1.0)]
+
+
+def _bits(vals):
+    from workloads import bf16_from_f32
+    return bf16_from_f32(np.asarray(vals, dtype=np.float32).reshape(-1, 1, 1))
+
+
+def test_extend_chunk_hand_worked_window_two():
+    """Values 10, 20, 30, 40, 50 at positions 0..4, a position-5 row of 1000
+    that no query may see, q = 0 (so the output is the mean of the visible
+    values).  Prefix 3, chunk 2: the queries sit at 3 and 4; with W = 2 they
+    see {2, 3} and {3, 4}: (30 + 40) / 2 = 35 and (40 + 50) / 2 = 45.  A chunk
+    placed one position early gives 25 and 35; a window taken as an inclusive
+    distance gives 30 and 40."""
+    c = LogicalCache(_scalar_layers(2), None, 1)
+    c.store(0, 0, 0, _bits([10, 20, 30, 40, 50, 1000]), _bits([10, 20, 30, 40, 50, 1000]))
+    out = c.extend(0, 0, _bits([0, 0]).reshape(2, 1, 1), 3)
+    assert out.shape == (2, 1, 1)
+    assert out[:, 0, 0].tolist() == [35.0, 45.0]
+
+
+def test_extend_chunk_hand_worked_full():
+    """Same rows, full causal layer: the queries at 3 and 4 see 0..3 and 0..4:
+    means 25 and 30.  The row at position 5 is cut."""
+    c = LogicalCache(_scalar_layers(0), None, 1)
+    c.store(0, 0, 0, _bits([10, 20, 30, 40, 50, 1000]), _bits([10, 20, 30, 40, 50, 1000]))
+    out = c.extend(0, 0, _bits([0, 0]).reshape(2, 1, 1), 3)
+    assert out[:, 0, 0].tolist() == [25.0, 30.0]
+
+
+def test_extend_chunk_of_tiny_workload_counts_its_keys():
+    """Tiny workload, chunk after the decode token: prefix 101, 64 queries at
+    101..164.  With q = 0 and value v_j = j, the query at p sees j in
+    [max(0, p - W + 1), p]: the mean is the midpoint of that range (W = 32:
+    p - 15.5; full: p / 2)."""
+    vals = np.arange(165, dtype=np.float32)
+    for window in (32, 0):
+        c = LogicalCache(_scalar_layers(window), None, 1)
+        c.store(0, 0, 0, _bits(vals), _bits(vals))
+        out = c.extend(0, 0, _bits(np.zeros(64)).reshape(64, 1, 1), 101)[:, 0, 0]
+        p = np.arange(101, 165, dtype=np.float64)
+        want = p - 15.5 if window else p / 2
+        assert np.array_equal(out, want), window
