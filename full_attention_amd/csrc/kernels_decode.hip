@@ -44,6 +44,8 @@
 // other keys are selected to -inf, and their value elements are selected to
 // zero before the product (slots that were never written may hold NaN).
 
+#include <mutex>
+
 #include "async_copy.h"
 #include "device_common.h"
 #include "launch_timing.h"
@@ -89,6 +91,9 @@ struct DecodeArgs {
     const uint16_t* k_new;
     const uint16_t* v_new;
     int32_t append;
+    // set by the call that uses the library's own scratch: the plan kernel
+    // zeroes the arrival counters of the call's units first
+    int32_t zero_arrivals;
 };
 
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
@@ -277,6 +282,11 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
     const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
     const int t = threadIdx.x;
     const int32_t B = a.num_seqs;
+    if (a.zero_arrivals) {
+        // the decode kernel runs after this kernel ends (stream order), and
+        // counts its arrivals from zero
+        for (int32_t i = blockIdx.x * 256 + t; i < B * a.hkv; i += gridDim.x * 256) a.arrivals[i] = 0u;
+    }
     build_seq_table(a, kv_lens, st, B);
     const int32_t T = st.soff[B];
     // the aligned split may lengthen the longest run by up to an eighth (at
@@ -1039,6 +1049,31 @@ __global__ __launch_bounds__(64) void xcd_probe_kernel(int32_t* out, int32_t n) 
 
 namespace pakv {
 
+// The workspace of pakv_paged_attn_decode_noalloc, for callers that cannot
+// allocate: one copy per GPU, held until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in); it takes
+// the device address from hipGetSymbolAddress, once per device.
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+int noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* per_device[kNoallocMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kNoallocMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // with `dev` current
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return 0;
+}
+
 int launch_xcd_probe(int32_t* out, int32_t n, void* stream) {
     hipLaunchKernelGGL(xcd_probe_kernel, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream), out, n);
     return (int)hipGetLastError();
@@ -1075,6 +1110,7 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.k_new = s.k_new;
     a.v_new = s.v_new;
     a.append = s.append;
+    a.zero_arrivals = s.zero_arrivals;
     return a;
 }
 

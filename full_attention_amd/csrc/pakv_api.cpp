@@ -450,6 +450,34 @@ pakv_status pakv_paged_attn_decode(const pakv_layer_map* map, int32_t layer, con
     return hip_status(launch_decode(a, stream), "paged_attn_decode launch");
 }
 
+pakv_status pakv_paged_attn_decode_noalloc(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                           const int32_t* kv_lens, const void* q, void* out,
+                                           int32_t num_seqs, int32_t max_kv_len, void* stream) {
+    clear_error();
+    DecodeLaunch a;
+    if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
+    if (num_seqs == 0) return PAKV_OK;
+    if (!kv_lens || !q || !out) return fail(PAKV_ERR_INVALID, "kv_lens, q or out is null");
+    const auto& d = map->layers[layer].desc;
+    const size_t need = decode_workspace_bytes(d, num_seqs, max_kv_len);
+    if (need > kNoallocScratchBytes)
+        return fail(PAKV_ERR_WORKSPACE,
+                    "decode needs %zu bytes of workspace, above the %zu of the library's scratch: "
+                    "call pakv_paged_attn_decode with a workspace", need, kNoallocScratchBytes);
+    void* ws = nullptr;
+    if (int e = noalloc_scratch(&ws)) return hip_status(e, "decode scratch address");
+    a.kv_lens = kv_lens;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    bind_partials(a, ws);
+    a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + decode_partial_bytes(d, num_seqs));
+    a.zero_arrivals = 1;
+    if (int e = launch_decode_plan(a, stream)) return hip_status(e, "decode_plan launch");
+    return hip_status(launch_decode(a, stream), "paged_attn_decode_noalloc launch");
+}
+
+size_t pakv_decode_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
 pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                    const int32_t* cu_q, const int32_t* prefix_lens,
                                    const void* q, void* out,

@@ -121,10 +121,19 @@ struct DecodeLaunch {
     const uint16_t* k_new = nullptr;   // append: [num_seqs][hkv][D] bf16, stored at kv_len - 1
     const uint16_t* v_new = nullptr;
     int32_t append = 0;
+    int32_t zero_arrivals = 0;   // the plan kernel zeroes the call's counters first
 };
 int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
 int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched
 int launch_xcd_probe(int32_t* out, int32_t n, void* stream);  // out[i] = XCD of workgroup i
+
+// The library's own decode workspace, for pakv_paged_attn_decode_noalloc: a
+// static device array of kNoallocScratchBytes on every GPU the library runs
+// on.  noalloc_scratch() returns the current device's address of it (taken
+// once per device with hipGetSymbolAddress); a hipError_t, 0 on success.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+constexpr int kNoallocMaxDevices = 64;
+int noalloc_scratch(void** ptr);
 
 struct ExtendLaunch {
     SlabView slab;

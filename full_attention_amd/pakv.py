@@ -33,6 +33,7 @@ EXPORTED = (
     "pakv_decode_plan_bytes", "pakv_decode_plan", "pakv_paged_attn_decode_planned",
     "pakv_paged_attn_decode_append",
     "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used", "pakv_workgroup_xcds",
+    "pakv_paged_attn_decode_noalloc", "pakv_decode_noalloc_max_bytes",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -92,6 +93,10 @@ lib.pakv_paged_attn_decode_planned.argtypes = [_P, _I, ctypes.POINTER(Pages), _P
 lib.pakv_paged_attn_decode_append.restype = _I
 lib.pakv_paged_attn_decode_append.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _S, _P, _P, _P, _P, _I, _I, _P, _S,
                                               _P]
+lib.pakv_paged_attn_decode_noalloc.restype = _I
+lib.pakv_paged_attn_decode_noalloc.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _I, _I, _P]
+lib.pakv_decode_noalloc_max_bytes.restype = _S
+lib.pakv_decode_noalloc_max_bytes.argtypes = []
 lib.pakv_paged_attn_extend.restype = _I
 lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
 lib.pakv_set_timing_events.restype = _I
@@ -233,6 +238,15 @@ def paged_attn_decode_append(layer_map, layer, pages, plan, plan_bytes, k_new, v
                                                     plan_bytes, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
                                                     num_seqs, max_kv_len, _ptr(workspace), workspace_bytes,
                                                     _stream(stream)))
+
+
+def paged_attn_decode_noalloc(layer_map, layer, pages, kv_lens, q, out, num_seqs, max_kv_len, stream=None):
+    return _check(lib.pakv_paged_attn_decode_noalloc(layer_map.handle, layer, ctypes.byref(pages), _ptr(kv_lens),
+                                                     _ptr(q), _ptr(out), num_seqs, max_kv_len, _stream(stream)))
+
+
+def decode_noalloc_max_bytes():
+    return lib.pakv_decode_noalloc_max_bytes()
 
 
 def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_seqs, total_q, max_q_len,

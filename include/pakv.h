@@ -269,6 +269,23 @@ pakv_status pakv_paged_attn_decode_append(const pakv_layer_map* map, int32_t lay
                                           int32_t num_seqs, int32_t max_kv_len,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* pakv_paged_attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The call allocates nothing: its
+ * plan, partials and arrival counters live in a static device array of the
+ * library, pakv_decode_noalloc_max_bytes() bytes (64 MiB) on each GPU it runs
+ * on, kept until the process ends.  Arguments and output as in
+ * pakv_paged_attn_decode (bit-identical results).  A call whose workspace
+ * (pakv_decode_workspace_bytes) would exceed that size returns
+ * PAKV_ERR_WORKSPACE before any launch.  Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must not be made; calls in one stream are fine.  The
+ * array's status word is not readable by the caller. */
+pakv_status pakv_paged_attn_decode_noalloc(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                           const int32_t* kv_lens, const void* q, void* out,
+                                           int32_t num_seqs, int32_t max_kv_len, void* stream);
+size_t pakv_decode_noalloc_max_bytes(void);
+
 /* Chunked prefill: a chunk of new queries per sequence after a cached prefix.
  *   cu_q        : device int32 [num_seqs + 1], prefix sums of chunk lengths n_b
  *   prefix_lens : device int32 [num_seqs]; query i of sequence b sits at

@@ -269,3 +269,24 @@ def test_workgroup_xcds_argument_errors_are_returned_before_launch():
     assert pakv.lib.pakv_workgroup_xcds(None, 8, None) == pakv.ERR_INVALID
     assert pakv.lib.pakv_workgroup_xcds(0x8000, 0, None) == pakv.ERR_INVALID
     assert pakv.lib.pakv_workgroup_xcds(0x8000, 65536, None) == pakv.ERR_INVALID
+
+
+def test_noalloc_decode_refuses_what_its_scratch_cannot_hold():
+    """pakv_paged_attn_decode_noalloc checks the workspace it would need against
+    its static scratch (64 MiB) before any GPU call; arguments as for decode."""
+    lib = pakv.lib
+    assert lib.pakv_decode_noalloc_max_bytes() == 64 << 20
+    m = pakv.LayerMap([_desc(d=512, hq=16, hkv=1)])
+    m.bind_slab(0, 0x1000, 0x2000, 8)
+    nseq, max_len = 1000, 1 << 17
+    pages = pakv.Pages(0x5000, nseq, max_len // 16)
+    need = lib.pakv_decode_workspace_bytes(m.handle, 0, nseq, max_len)
+    assert need > 64 << 20
+    st = lib.pakv_paged_attn_decode_noalloc(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x7000, nseq,
+                                            max_len, None)
+    assert st == pakv.ERR_WORKSPACE and "scratch" in pakv.last_error()
+    # the decode checks come first
+    assert lib.pakv_paged_attn_decode_noalloc(m.handle, 0, ctypes.byref(pages), None, 0x6100, 0x7000, 2, 40,
+                                              None) == pakv.ERR_INVALID
+    assert lib.pakv_paged_attn_decode_noalloc(m.handle, 0, ctypes.byref(pages), None, None, None, 0, 40,
+                                              None) == pakv.OK
