@@ -18,6 +18,9 @@ What it computes, and the pages each part follows:
                    fixed by the bytes-per-token figures in "End to end").  The
                    rounding and the clamp are this oracle's reading; the pages
                    do not print them.
+* ``fp8_pth``   -- the fp8 per-token-head sibling format (same bullet; same
+                   D + 4 bytes per row): E4M3 codes, scale amax / 448, round
+                   to nearest even, saturating (this oracle's reading).
 * ``attention`` -- dense attention in float64 over an explicitly materialised
                    visibility mask (full causal, or causal and inside a window
                    of W positions that counts the query's own position),
@@ -25,7 +28,10 @@ What it computes, and the pages each part follows:
                    and pegainfer issue #807 (Description: the window_left
                    conversion).
 * ``cache``     -- logical, position-ordered K/V arrays per owning layer and
-                   sequence: what a paged cache holds, without pages.
+                   sequence: what a paged cache holds, without pages; K=V
+                   layers (value = RMS-normalised key, unsloth commit 749fb75)
+                   and extend chunks given as packed rows (FreeToken PR #898,
+                   description, fourth bullet).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against values the pages print, closed forms, brute force and a library
@@ -34,12 +40,14 @@ routine; none is "parity unpinned".
 
 from .attention import visibility_mask, attend, decode_positions, extend_positions
 from .int8_pth import quantise_rows, dequantise_rows
+from . import fp8_pth
+from .fp8_pth import e4m3_encode, e4m3_value
 from .layers import kv_sources, owner_layers, kv_bytes_per_token, AliasError
-from .cache import LogicalCache
+from .cache import LogicalCache, v_from_k
 
 __all__ = [
     "visibility_mask", "attend", "decode_positions", "extend_positions",
-    "quantise_rows", "dequantise_rows",
+    "quantise_rows", "dequantise_rows", "fp8_pth", "e4m3_encode", "e4m3_value", "v_from_k",
     "kv_sources", "owner_layers", "kv_bytes_per_token", "AliasError",
     "LogicalCache",
 ]

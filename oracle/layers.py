@@ -49,7 +49,8 @@ def kv_bytes_per_token(layer_types, first_shared, head_dim, kv_heads, fmt="bf16"
     """(full_bytes, window_bytes) per token over owning layers.
 
     head_dim / kv_heads map an attention type ("full" or "sliding") to D / Hkv.
-    fmt is "bf16" or "int8" (one 4-byte scale per token-head row).
+    fmt is "bf16", or "int8" / "fp8" (8-bit codes and one 4-byte scale per
+    token-head row).
     """
     totals = {"full": 0, "sliding": 0}
     for layer in owner_layers(layer_types, first_shared, share):

@@ -156,3 +156,80 @@ def test_extend_chunk_of_tiny_workload_counts_its_keys():
         p = np.arange(101, 165, dtype=np.float64)
         want = p - 15.5 if window else p / 2
         assert np.array_equal(out, want), window
+
+
+# ---- K=V layers (value = RMS-normalised key) and packed extend chunks -------
+
+from oracle import v_from_k
+
+
+def _kv_layer(d, eps, fmt="bf16", window=0):
+    return dict(type="sliding" if window else "full", head_dim=d, num_q_heads=1, num_kv_heads=1,
+                window=window, kv_dtype=fmt, sm_scale=1.0, k_eq_v=True, v_norm_eps=eps)
+
+
+def test_v_from_k_closed_forms():
+    # mean of squares 25 -> root 5: [1, 7] / 5
+    assert v_from_k(np.array([[1.0, 7.0]]), 0.0).tolist() == [[0.2, 1.4]]
+    # a constant row normalises to ones (sign kept); a one-hot row to sqrt(D)
+    assert v_from_k(np.array([[-3.0, -3.0, -3.0, -3.0]]), 0.0).tolist() == [[-1.0] * 4]
+    assert v_from_k(np.array([[0.0, 2.0, 0.0, 0.0]]), 0.0).tolist() == [[0.0, 2.0, 0.0, 0.0]]
+    # eps sits under the root: [1, 7] with eps 1 -> [1, 7] / sqrt(26)
+    assert np.allclose(v_from_k(np.array([[1.0, 7.0]]), 1.0), np.array([[1.0, 7.0]]) / np.sqrt(26.0), rtol=1e-15)
+    # scale invariance when eps = 0, and unit mean square
+    k = np.random.default_rng(0).standard_normal((5, 64))
+    assert np.allclose(v_from_k(3.5 * k, 0.0), v_from_k(k, 0.0), rtol=1e-13)
+    assert np.allclose(np.mean(v_from_k(k, 0.0) ** 2, axis=-1), 1.0, rtol=1e-13)
+
+
+def test_k_eq_v_layer_stores_keys_only_and_derives_values():
+    """D = 2, q = 0: the decode output is the mean of the visible value rows.
+    Keys [1, 7] and [5, 5] (eps 0) give values [0.2, 1.4] and [1, 1]: the
+    query at position 1 sees both, mean [0.6, 1.2]; a shared layer reads the
+    same rows."""
+    layers = [_kv_layer(2, 0.0), dict(_kv_layer(2, 0.0))]
+    c = LogicalCache(layers, 1, 1)
+    k = _bits([[1.0, 7.0], [5.0, 5.0]]).reshape(2, 1, 2)
+    c.store(0, 0, 0, k, None)
+    pos, rows = c.stored(0, 0)
+    assert all(r[1] is None for r in rows)          # no value rows kept
+    q = _bits([0.0, 0.0]).reshape(1, 2)
+    out = c.decode(0, 0, q, 2)
+    assert np.allclose(out[0], [0.6, 1.2], rtol=1e-15)
+    assert np.array_equal(c.decode(1, 0, q, 2), out)
+
+
+def test_k_eq_v_int8_layer_normalises_the_decoded_key():
+    """int8 K=V: the value is the decoded key row, normalised.  Key [127, -127]
+    quantises exactly (scale 1), so its value is [1, -1] (eps 0)."""
+    c = LogicalCache([_kv_layer(2, 0.0, fmt="int8")], None, 1)
+    c.store(0, 0, 0, _bits([[127.0, -127.0]]).reshape(1, 1, 2), None)
+    out = c.decode(0, 0, _bits([0.0, 0.0]).reshape(1, 2), 1)
+    assert out[0].tolist() == [1.0, -1.0]
+
+
+def test_extend_packed_takes_the_chunk_as_given():
+    """D = 1, q = 0.  Stored 10, 20, 30 at positions 0..2 and a stale 1000 at 3;
+    the chunk at prefix 3 comes as packed rows 40, 50: the queries at 3 and 4
+    see (10 + 20 + 30 + 40) / 4 = 25 and 30.  The stored row at position 3
+    is not used."""
+    c = LogicalCache(_scalar_layers(0), None, 1)
+    c.store(0, 0, 0, _bits([10, 20, 30, 1000]), _bits([10, 20, 30, 1000]))
+    out = c.extend_packed(0, 0, _bits([0, 0]).reshape(2, 1, 1), 3, _bits([40, 50]), _bits([40, 50]))
+    assert out[:, 0, 0].tolist() == [25.0, 30.0]
+    # no prefix at all
+    c2 = LogicalCache(_scalar_layers(2), None, 1)
+    out = c2.extend_packed(0, 0, _bits([0, 0, 0]).reshape(3, 1, 1), 0, _bits([4, 8, 16]), _bits([4, 8, 16]))
+    assert out[:, 0, 0].tolist() == [4.0, 6.0, 12.0]
+
+
+def test_extend_packed_chunk_stays_exact_over_an_int8_prefix():
+    """An int8 cache: the stored prefix is decoded (127 and 254 quantise to code
+    127 with scales 1 and 2, exactly), the packed chunk row 3 is taken as given
+    (bf16, not quantised): means (127 + 254 + 3) / 3 = 128."""
+    layers = [dict(type="full", head_dim=1, num_q_heads=1, num_kv_heads=1, window=0, kv_dtype="int8",
+                   sm_scale=1.0)]
+    c = LogicalCache(layers, None, 1)
+    c.store(0, 0, 0, _bits([127, 254]), _bits([127, 254]))
+    out = c.extend_packed(0, 0, _bits([0]).reshape(1, 1, 1), 2, _bits([3]), _bits([3]))
+    assert out[0, 0, 0] == 128.0
