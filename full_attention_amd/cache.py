@@ -20,10 +20,22 @@ class PagedKVCache:
     num_kv_heads, window (0 = full), kv_dtype ("bf16" / "int8") and sm_scale.
     first_shared: index of the first KV-shared layer, or None."""
 
-    def __init__(self, layers, first_shared, num_pages, device="cuda", sentinel=True):
-        get = (lambda l, k: l[k]) if isinstance(layers[0], dict) else (lambda l, k: getattr(l, k))
+    DTYPES = {"bf16": pakv.KV_BF16, "int8": pakv.KV_INT8_PTH, "fp8": pakv.KV_FP8_PTH}
+
+    def __init__(self, layers, first_shared, num_pages, device="cuda", sentinel=True, k_eq_v_storage=True,
+                 v_norm_eps=1e-6):
+        """k_eq_v_storage: layers whose spec says k_eq_v keep one slab (values
+        derived from the keys in-kernel); False keeps two slabs and the caller
+        stores the value rows itself."""
+        def get(l, k, default=None):
+            if isinstance(l, dict):
+                return l.get(k, default)
+            return getattr(l, k, default)
         self.specs = [{k: get(l, k) for k in ("head_dim", "num_q_heads", "num_kv_heads", "window",
                                               "kv_dtype", "sm_scale")} for l in layers]
+        for s, l in zip(self.specs, layers):
+            s["k_eq_v"] = bool(get(l, "k_eq_v", False)) and k_eq_v_storage
+            s["v_norm_eps"] = float(v_norm_eps)
         n = len(self.specs)
         types = [SLIDING if s["window"] > 0 else FULL for s in self.specs]
         fs = n if first_shared is None else first_shared
@@ -32,8 +44,8 @@ class PagedKVCache:
         for l, s in enumerate(self.specs):
             descs.append(pakv.LayerDesc(s["head_dim"], s["num_q_heads"], s["num_kv_heads"], s["window"],
                                         -1 if self.sources[l] == l else self.sources[l],
-                                        pakv.KV_BF16 if s["kv_dtype"] == "bf16" else pakv.KV_INT8_PTH,
-                                        float(s["sm_scale"])))
+                                        self.DTYPES[s["kv_dtype"]], float(s["sm_scale"]),
+                                        1 if s["k_eq_v"] else 0, s["v_norm_eps"]))
         self.map = pakv.LayerMap(descs)
         self.num_pages = num_pages
         self.device = torch.device(device)
@@ -45,10 +57,12 @@ class PagedKVCache:
             if s["kv_dtype"] == "bf16":
                 fill = 0x7FC0 if sentinel else 0            # bf16 quiet NaN
                 k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int16, device=self.device)
-                v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int16, device=self.device)
+                v = None if s["k_eq_v"] else torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int16,
+                                                        device=self.device)
                 ks = vs = None
             else:
-                fill = -128 if sentinel else 0
+                # int8: -128, a code the encoder never makes; fp8: 0xFF, an E4M3 NaN
+                fill = (-128 if s["kv_dtype"] == "int8" else -1) if sentinel else 0
                 k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int8, device=self.device)
                 v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int8, device=self.device)
                 sfill = float("nan") if sentinel else 0.0
@@ -68,7 +82,7 @@ class PagedKVCache:
         self.page_table = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
         self.pages = pakv.make_pages(self.page_table)
 
-    def store(self, layer, cu_tokens, start_pos, k, v, stream=None):
+    def store(self, layer, cu_tokens, start_pos, k, v=None, stream=None):
         total = k.shape[0]
         nseq = cu_tokens.shape[0] - 1
         pakv.paged_kv_store(self.map, layer, self.pages, cu_tokens, start_pos, k, v, nseq, total, stream)
@@ -140,4 +154,15 @@ class PagedKVCache:
             out = torch.empty_like(q)
         pakv.paged_attn_extend(self.map, layer, self.pages, cu_q, prefix_lens, q, out, nseq, q.shape[0],
                                max_q_len, max_kv_len, stream)
+        return out
+
+    def extend_packed(self, layer, cu_q, prefix_lens, q, k_ext, v_ext, max_q_len, max_kv_len, out=None,
+                      stream=None):
+        """Extend with the chunk's own rows given as packed tensors (v_ext None
+        for a K=V layer); only the prefix is read from the slab."""
+        nseq = cu_q.shape[0] - 1
+        if out is None:
+            out = torch.empty_like(q)
+        pakv.paged_attn_extend_packed(self.map, layer, self.pages, cu_q, prefix_lens, q, k_ext, v_ext, out, nseq,
+                                      q.shape[0], max_q_len, max_kv_len, stream)
         return out

@@ -84,4 +84,14 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t word, int byte_lo) {
     return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+// fp8 (OCP E4M3) code pair -> bf16 pair bits: bytes 0, 1 (byte_lo 0) or 2, 3
+// (byte_lo 2) of word.  Exact: every E4M3 value, subnormals included, has a
+// bf16 twin (3 mantissa bits, exponents 2^-9 .. 2^8), so the float32 the
+// conversion instruction gives keeps only its top half.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word, int byte_lo) {
+    const f32x2 f = byte_lo == 2 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true)
+                                 : __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+}
+
 }  // namespace pakv_dev

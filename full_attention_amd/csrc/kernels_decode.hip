@@ -94,6 +94,7 @@ struct DecodeArgs {
     // set by the call that uses the library's own scratch: the plan kernel
     // zeroes the arrival counters of the call's units first
     int32_t zero_arrivals;
+    float v_norm_eps;       // K=V layers: eps under the root of the value norm
 };
 
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
@@ -106,25 +107,34 @@ __device__ __forceinline__ void wait_chunks(int newer) {
     wait_vm<0>();
 }
 
-template <int D, bool INT8>
+// KV formats of the decode kernel (template argument F): bf16 K and V slabs;
+// int8 or fp8 (E4M3) codes with a float32 scale per token and head; bf16 K
+// only, the values being the RMS-normalised keys (K=V layers).
+constexpr int kFmtBF16 = 0, kFmtINT8 = 1, kFmtFP8 = 2, kFmtKEQV = 3;
+
+template <int D, int F>
 struct Cfg {
-    static constexpr int ES = INT8 ? 1 : 2;                 // bytes per code
+    static constexpr bool Q8 = F == kFmtINT8 || F == kFmtFP8;   // 8-bit codes with scales
+    static constexpr bool HAS_V = F != kFmtKEQV;             // a V slab to copy
+    static constexpr int ES = Q8 ? 1 : 2;                   // bytes per code
     static constexpr int ROW = D * ES;                      // bytes per K row
     static constexpr int PAGE = 16 * D * ES;                // bytes per (page, head) block
-    static constexpr int SCALE_BYTES = INT8 ? 128 : 0;      // k and v scales of one page
-    static constexpr int BUF = 2 * PAGE + SCALE_BYTES;
+    static constexpr int SCALE_BYTES = Q8 ? 128 : 0;        // k and v scales of one page
+    static constexpr int BUF = (HAS_V ? 2 : 1) * PAGE + SCALE_BYTES;
     // ring slots: bf16 pages copied one ahead (two slots); a deeper ring
     // (three or four slots at D = 256) was slower in the step: with every
     // workgroup streaming, more requests in flight only lengthen the queues
     // and the stragglers.  int8 pages are half the bytes: four slots.
-    static constexpr int NBUF = INT8 ? 4 : 2;
-    static constexpr int KV_DMA = 2 * PAGE / (1024 * kWaves);   // copies per wave per chunk
-    static constexpr int PER = KV_DMA + (INT8 ? 1 : 0);
-    static constexpr int SX = kWaves * 64 * 16;             // partial-score exchange
+    static constexpr int NBUF = Q8 ? 4 : 2;
+    static constexpr int KV_DMA = (HAS_V ? 2 : 1) * PAGE / (1024 * kWaves);   // copies per wave per chunk
+    static constexpr int PER = KV_DMA + (Q8 ? 1 : 0);
+    // partial-score exchange (and, for K=V, each wave's partial sums of
+    // squares of the 16 key rows)
+    static constexpr int SX = kWaves * 64 * 16 + (HAS_V ? 0 : kWaves * 16 * 4);
     static constexpr int SEQ = (2 * (pakv::kDecodeMaxSeqs + 1) * 4 + 15) & ~15;   // per-sequence table
     // append: per ring slot, the new V row (D bf16) and the page id it goes to
-    static constexpr int STAGE = INT8 ? 0 : D * 2;
-    static constexpr int NEWP = INT8 ? 0 : 16;
+    static constexpr int STAGE = F == kFmtBF16 ? D * 2 : 0;
+    static constexpr int NEWP = F == kFmtBF16 ? 16 : 0;
     static constexpr int LDS = NBUF * BUF + SX + SEQ + NBUF * STAGE + NEWP;
     static constexpr int KK = D / 128;                      // 32-dim steps in a wave's quarter
     static constexpr int MT = D / 64;                       // 16-dim output tiles in a quarter
@@ -414,10 +424,10 @@ __device__ __forceinline__ void take_q(u32x4 (&qreg)[N], bool real) {
 // PER / 2 of V for the chunk, and the staging copy comes before them, so the
 // waits for a chunk's K and for its V still cover everything (they can only
 // wait for one copy more than needed).
-template <int D, bool INT8>
+template <int D, int F>
 __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, uint32_t raw_id, uint8_t* buf, const Unit& x,
                                             bool last, uint8_t* stage, int32_t* newp, int wave, int lane) {
-    using C = Cfg<D, INT8>;
+    using C = Cfg<D, F>;
     // an id outside the pool (a missing page or a stale plan) reads page 0
     const bool in_pool = raw_id < (uint32_t)a.num_pages;
     const int32_t phys = in_pool ? (int32_t)raw_id : 0;
@@ -425,7 +435,7 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, uint32_t raw_id
     const uint8_t* kp = a.k_slab + blk;       // wave-uniform bases; per-lane 32-bit offsets
     const uint8_t* vp = a.v_slab + blk;
     const uint32_t kb = lds_addr_of(buf), vb = kb + C::PAGE;
-    if constexpr (!INT8) {
+    if constexpr (F == kFmtBF16) {
         if (a.append && last) {
             const int64_t nrow = ((int64_t)x.b * a.hkv + x.g) * D;     // the (b, g) row of k_new / v_new
             const int r = (x.hi - 1) & 15;                              // slot of position L - 1
@@ -467,17 +477,19 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, uint32_t raw_id
     // V: the dim-major page block; for bf16 the two 16-byte halves of dim d
     // trade places when bit 3 of d is set, so that the 16 dims read at once
     // land in different bank groups
+    if constexpr (C::HAS_V) {
 #pragma unroll
-    for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
-        const int inst = wave + kWaves * i;
-        if constexpr (!INT8) {
-            const int gp = inst * 64 + lane, d = gp >> 1;
-            dma16_s_nt(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
-        } else {
-            dma16_s_nt(vp, (uint32_t)(inst * 1024 + lane * 16), vb + inst * 1024);
+        for (int i = 0; i < C::PAGE / 1024 / kWaves; ++i) {
+            const int inst = wave + kWaves * i;
+            if constexpr (!C::Q8) {
+                const int gp = inst * 64 + lane, d = gp >> 1;
+                dma16_s_nt(vp, (uint32_t)(d * 32 + (((gp & 1) ^ ((d >> 3) & 1)) * 16)), vb + inst * 1024);
+            } else {
+                dma16_s_nt(vp, (uint32_t)(inst * 1024 + lane * 16), vb + inst * 1024);
+            }
         }
     }
-    if constexpr (INT8) {
+    if constexpr (C::Q8) {
         // wave w copies 32 bytes of the page's 128 bytes of scales (k then v)
         if (lane < 2) {
             const int seg = wave * 2 + lane;                  // 16-byte piece 0..7
@@ -711,9 +723,16 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Unit& x, i
     }
 }
 
-template <int D, bool INT8>
+// Two 8-bit codes of a word -> a bf16 pair (exact), for the 8-bit formats.
+template <int F>
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t word, int byte_lo) {
+    if constexpr (F == kFmtFP8) return fp8x2_to_bf16x2(word, byte_lo);
+    else return i8x2_to_bf16x2(word, byte_lo);
+}
+
+template <int D, int F>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
-    using C = Cfg<D, INT8>;
+    using C = Cfg<D, F>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     __shared__ uint32_t ticket;
     f32x4* sx = reinterpret_cast<f32x4*>(lds + C::NBUF * C::BUF);
@@ -795,7 +814,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < C::NBUF - 1; ++c) {
         if (c < total) {
-            issue_chunk<D, INT8>(a, (uint32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui,
+            issue_chunk<D, F>(a, (uint32_t)__builtin_amdgcn_readlane(ids, c), lds + c * C::BUF, ui,
                                  ki == ui.n - 1, stage + c * C::STAGE, newp + c, wave, lane);
             advance(a, st, U, ui, ki);
         }
@@ -809,9 +828,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     for (int32_t i = 0; i < total; ++i) {
         // bf16: this chunk's K only (each wave issues K before V); its V is
         // awaited after the scores, so the score product overlaps V's arrival
-        // (with one chunk ahead, only this chunk's copies are in flight here)
-        static_assert(INT8 || C::NBUF == 2, "the split K / V waits count one chunk in flight");
-        if constexpr (!INT8) wait_vm<C::PER / 2>();
+        // (with one chunk ahead, only this chunk's copies are in flight here).
+        // K=V: the chunk's copies are all K.
+        static_assert(C::Q8 || C::NBUF == 2, "the split K / V waits count one chunk in flight");
+        if constexpr (F == kFmtBF16) wait_vm<C::PER / 2>();
+        else if constexpr (F == kFmtKEQV) wait_vm<0>();
         else wait_chunks<C::PER, C::NBUF>(min(C::NBUF - 2, total - 1 - i));
         lds_barrier();
         if (kc == 0 || i == 0) {
@@ -829,7 +850,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                     ids = sched_ids(a, c_begin + j, min(total - j, 64), lane);
                     wait_vm<0>();
                 }
-                issue_chunk<D, INT8>(a, (uint32_t)__builtin_amdgcn_readlane(ids, j & 63),
+                issue_chunk<D, F>(a, (uint32_t)__builtin_amdgcn_readlane(ids, j & 63),
                                      lds + (j % C::NBUF) * C::BUF, ui, ki == ui.n - 1,
                                      stage + (j % C::NBUF) * C::STAGE, newp + (j % C::NBUF), wave, lane);
                 advance(a, st, U, ui, ki);
@@ -838,7 +859,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         const uint8_t* kbuf = lds + (i % C::NBUF) * C::BUF;
         const uint8_t* vbuf = kbuf + C::PAGE;
         const int32_t t0 = (uc.page0 + kc) * kChunk;
-        if constexpr (!INT8) {
+        if constexpr (F == kFmtBF16) {
             if (a.append && kc == uc.n - 1) {
                 // the new token (slot r of this page): write its K row (already
                 // in LDS, from k_new) and its staged V values to the slab; the V
@@ -866,6 +887,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
         // ---- partial scores over this wave's dim quarter --------------------
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;     // K=V: this lane's part of the key row's sum of squares
         {
             const int row = col;
             const uint8_t* krow = kbuf + row * C::ROW;
@@ -873,17 +895,31 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             for (int kk = 0; kk < C::KK; ++kk) {
                 const int e0 = dq + 32 * kk + 8 * qg;          // first of 8 dims
                 u32x4 ka;
-                if constexpr (!INT8) {
+                if constexpr (!C::Q8) {
                     ka = *reinterpret_cast<const u32x4*>(krow + (((e0 >> 3) ^ (row & 15)) * 16));
+                    if constexpr (F == kFmtKEQV) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const float lo = __uint_as_float(ka[w] << 16), hi = __uint_as_float(ka[w] & 0xffff0000u);
+                            ss = __builtin_fmaf(lo, lo, ss);
+                            ss = __builtin_fmaf(hi, hi, ss);
+                        }
+                    }
                 } else {
                     const u32x2 w = *reinterpret_cast<const u32x2*>(krow + (((e0 >> 4) ^ (row & 15)) * 16) + (e0 & 8));
-                    ka = u32x4{i8x2_to_bf16x2(w.x, 0), i8x2_to_bf16x2(w.x, 2),
-                               i8x2_to_bf16x2(w.y, 0), i8x2_to_bf16x2(w.y, 2)};
+                    ka = u32x4{codes_to_bf16x2<F>(w.x, 0), codes_to_bf16x2<F>(w.x, 2),
+                               codes_to_bf16x2<F>(w.y, 0), codes_to_bf16x2<F>(w.y, 2)};
                 }
                 acc = mfma_16x16x32(ka, qreg[kk], acc);
             }
         }
-        if constexpr (!INT8) {
+        float* ssx = reinterpret_cast<float*>(sx + kWaves * 64);   // K=V: [wave][16 rows]
+        if constexpr (F == kFmtKEQV) {
+            // the four 16-lane rows hold four dim groups of key row `col`
+            ss = wave_sum_across_groups(ss);
+            if (qg == 0) ssx[wave * 16 + col] = ss;
+        }
+        if constexpr (F == kFmtBF16) {
             // this chunk's V: past it, only the next chunk's copies (issued at
             // the top of this step) may still be in flight
             if (i + 1 < total) wait_vm<C::PER>();
@@ -891,7 +927,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         }
         sx[wave * 64 + lane] = acc;
         lds_barrier();
-        if constexpr (!INT8) {
+        if constexpr (F == kFmtBF16) {
             if (a.append && kc == uc.n - 1) {
                 // every wave's V copies have landed: patch in the new token's V
                 // (two bytes per dim, each dim's 32 bytes copied by one wave)
@@ -910,12 +946,24 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
         // ---- online softmax: lane holds tokens t0 + 4*qg + i -----------------
         float ks[4] = {1.f, 1.f, 1.f, 1.f}, vs[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (INT8) {
+        if constexpr (C::Q8) {
             const float* scl = reinterpret_cast<const float*>(vbuf + C::PAGE);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 ks[e] = scl[4 * qg + e];
                 vs[e] = scl[16 + 4 * qg + e];
+            }
+        }
+        if constexpr (F == kFmtKEQV) {
+            // value row = key row / sqrt(mean square + eps): the factor goes
+            // into the weights, the key row itself into the value product
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * qg + e;
+                float t = ssx[r];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) t += ssx[w * 16 + r];
+                vs[e] = __builtin_amdgcn_rsqf(t * (1.0f / D) + a.v_norm_eps);
             }
         }
         float sc[4];
@@ -926,7 +974,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             const int32_t t = t0 + 4 * qg + e;
             valid[e] = (t >= uc.lo) && (t < uc.hi);
             float v = tot[e] * a.score_scale;
-            if constexpr (INT8) v *= ks[e];
+            if constexpr (C::Q8) v *= ks[e];
             sc[e] = valid[e] ? v : -INFINITY;
             mx = fmaxf(mx, sc[e]);
         }
@@ -948,7 +996,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float x = p[e];
-            if constexpr (INT8) x *= vs[e];
+            if constexpr (F != kFmtBF16) x *= vs[e];
             pv[e] = valid[e] ? x : 0.0f;
         }
         const u32x2 pb = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
@@ -959,15 +1007,33 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         for (int m = 0; m < C::MT; ++m) {
             const int d = dq + 16 * m + col;
             u32x2 va;
-            if constexpr (!INT8) {
+            if constexpr (F == kFmtBF16) {
                 va = *reinterpret_cast<const u32x2*>(vbuf + d * 32 + ((((qg >> 1) ^ (d >> 3)) & 1) << 4) + 8 * (qg & 1));
-                if (!full) {
-                    va.x &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
-                    va.y &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+            } else if constexpr (F == kFmtKEQV) {
+                // the value operand (one dim, four tokens) from the key rows:
+                // token 4 qg + e's 2-byte element d, in granule (d / 8) ^ token.
+                // (The lane index is made opaque per tile, so that these
+                // addresses are formed where they are read instead of being
+                // held in registers across the chunk loop.)
+                int lid = lane;
+                asm volatile("" : "+v"(lid));
+                const int dd = dq + 16 * m + (lid & 15), rq = 4 * (lid >> 4);
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = rq + e;
+                    h[e] = *reinterpret_cast<const uint16_t*>(kbuf + r * C::ROW + ((((dd >> 3) ^ r) & (C::ROW / 16 - 1)) << 4) +
+                                                              (dd & 7) * 2);
                 }
+                va = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
             } else {
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(vbuf + d * 16 + 4 * qg);
-                va = u32x2{i8x2_to_bf16x2(w, 0), i8x2_to_bf16x2(w, 2)};
+                va = u32x2{codes_to_bf16x2<F>(w, 0), codes_to_bf16x2<F>(w, 2)};
+            }
+            // slots outside the visible range may hold NaN (int8 codes cannot)
+            if (F != kFmtINT8 && !full) {
+                va.x &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+                va.y &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
             }
             o[m] = o[m] * alpha;
             o[m] = mfma_16x16x16(va, pb, o[m]);
@@ -1111,6 +1177,7 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.v_new = s.v_new;
     a.append = s.append;
     a.zero_arrivals = s.zero_arrivals;
+    a.v_norm_eps = s.v_norm_eps;
     return a;
 }
 
@@ -1125,14 +1192,24 @@ int launch_decode(const DecodeLaunch& s, void* stream) {
     const DecodeArgs a = args_of(s);
     hipStream_t st = static_cast<hipStream_t>(stream);
     dim3 grid1(s.plan.grid);
-    const bool i8 = s.kv_dtype == PAKV_KV_INT8_PTH;
+    const int f = s.k_eq_v ? kFmtKEQV
+                           : (s.kv_dtype == PAKV_KV_INT8_PTH ? kFmtINT8 : (s.kv_dtype == PAKV_KV_FP8_PTH ? kFmtFP8 : kFmtBF16));
     const int K = PAKV_TIME_DECODE;
+    const dim3 blk(256);
     if (s.head_dim == 256) {
-        if (i8) launch(K, decode_kernel<256, true>, grid1, dim3(256), 0, st, a);
-        else launch(K, decode_kernel<256, false>, grid1, dim3(256), 0, st, a);
+        switch (f) {
+            case kFmtINT8: launch(K, decode_kernel<256, kFmtINT8>, grid1, blk, 0, st, a); break;
+            case kFmtFP8: launch(K, decode_kernel<256, kFmtFP8>, grid1, blk, 0, st, a); break;
+            case kFmtKEQV: launch(K, decode_kernel<256, kFmtKEQV>, grid1, blk, 0, st, a); break;
+            default: launch(K, decode_kernel<256, kFmtBF16>, grid1, blk, 0, st, a); break;
+        }
     } else {
-        if (i8) launch(K, decode_kernel<512, true>, grid1, dim3(256), 0, st, a);
-        else launch(K, decode_kernel<512, false>, grid1, dim3(256), 0, st, a);
+        switch (f) {
+            case kFmtINT8: launch(K, decode_kernel<512, kFmtINT8>, grid1, blk, 0, st, a); break;
+            case kFmtFP8: launch(K, decode_kernel<512, kFmtFP8>, grid1, blk, 0, st, a); break;
+            case kFmtKEQV: launch(K, decode_kernel<512, kFmtKEQV>, grid1, blk, 0, st, a); break;
+            default: launch(K, decode_kernel<512, kFmtBF16>, grid1, blk, 0, st, a); break;
+        }
     }
     return (int)hipGetLastError();
 }

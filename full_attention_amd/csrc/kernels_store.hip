@@ -1,10 +1,13 @@
 // paged_kv_store: scatter new K/V rows into a layer's slab.
 //
 // One wavefront per (token, KV head) row.  bf16 rows are copied bit for bit;
-// int8 per-token-head rows are encoded in-kernel: amax over the row, one IEEE
-// float32 division for the scale, one per element, round half to even, clamp
-// to +-127 (the library's reading of the per-token-head format described in
-// FreeToken PR #898, description bullet on the 8-bit formats).
+// 8-bit per-token-head rows are encoded in-kernel (the library's reading of
+// the per-token-head formats described in FreeToken PR #898, description
+// bullet on the 8-bit formats): amax over the row, one IEEE float32 division
+// for the scale (amax / 127 for int8, amax / 448 for fp8), one per element,
+// then round half to even: to an integer clamped to +-127 (int8), or to the
+// nearest OCP E4M3 value, saturating at +-448 (fp8).  A K=V layer (values
+// derived from the keys when read) stores its K rows only.
 //
 // K pages are token-major ([16][D]); V pages are dim-major ([D][16]), so a V
 // row lands as D strided 2-byte (or 1-byte) stores.
@@ -28,7 +31,7 @@ struct StoreArgs {
     const int32_t* cu_tokens;
     const int32_t* start_pos;
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* v;      // null for a K=V layer: nothing is stored for V
     int32_t num_seqs;
     int32_t total_tokens;
     int32_t hkv;
@@ -76,13 +79,14 @@ __global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
     if (t >= a.total_tokens) return;
     // the row itself does not depend on where it goes: fetch it first
     const int64_t src = ((int64_t)t * a.hkv + h) * D + lane * EPL;
+    const bool has_v = a.v != nullptr;
     uint16_t kv[EPL], vv[EPL];
     if constexpr (EPL == 8) {
         *reinterpret_cast<u32x4*>(kv) = *reinterpret_cast<const u32x4*>(a.k + src);
-        *reinterpret_cast<u32x4*>(vv) = *reinterpret_cast<const u32x4*>(a.v + src);
+        if (has_v) *reinterpret_cast<u32x4*>(vv) = *reinterpret_cast<const u32x4*>(a.v + src);
     } else {
         *reinterpret_cast<u32x2*>(kv) = *reinterpret_cast<const u32x2*>(a.k + src);
-        *reinterpret_cast<u32x2*>(vv) = *reinterpret_cast<const u32x2*>(a.v + src);
+        if (has_v) *reinterpret_cast<u32x2*>(vv) = *reinterpret_cast<const u32x2*>(a.v + src);
     }
     int64_t ph;
     int32_t slot;
@@ -90,22 +94,52 @@ __global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
     uint16_t* kdst = reinterpret_cast<uint16_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
     if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(kdst) = *reinterpret_cast<u32x4*>(kv);
     else *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kv);
+    if (!has_v) return;
     uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_slab) + ph * kPage * D + slot;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) vdst[(lane * EPL + e) * kPage] = vv[e];
 }
 
-// Encodes EPL bf16 values of one lane into int8 codes given the row's scale.
-template <int EPL>
-__device__ __forceinline__ void encode(const float (&x)[EPL], float scale, int8_t (&code)[EPL]) {
+// Nearest OCP E4M3 code of y (ties to even mantissa), saturating at +-448:
+// below 2^-6 the grid is the multiples of 2^-9 (y * 512 is exact, and a
+// result of 8 is the first normal code); above, y = f * 2^e with f in [1, 2)
+// keeps rint((f - 1) * 8) as its 3-bit mantissa, carrying into the exponent
+// at 8.  Written from the format's definition; v_rndne_f32 rounds half to even.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+    int e = (int)((u >> 23) & 0xffu) - 127;
+    const float f = __uint_as_float((u & 0x007fffffu) | 0x3f800000u);
+    int q = (int)__builtin_rintf((f - 1.0f) * 8.0f);
+    if (q == 8) {
+        ++e;
+        q = 0;
+    }
+    if (e > 8 || (e == 8 && q > 6)) {
+        e = 8;
+        q = 6;
+    }
+    return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)q;
+}
+
+// Encodes EPL bf16 values of one lane into 8-bit codes given the row's scale
+// (an all-zero row, scale 0, gets zero codes).
+template <int EPL, bool FP8>
+__device__ __forceinline__ void encode(const float (&x)[EPL], float scale, uint8_t (&code)[EPL]) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        float c = 0.0f;
-        if (scale > 0.0f) {
-            c = __builtin_rintf(x[e] / scale);
-            c = fminf(fmaxf(c, -127.0f), 127.0f);
+        if constexpr (FP8) {
+            code[e] = scale > 0.0f ? (uint8_t)e4m3_code(x[e] / scale) : (uint8_t)0;
+        } else {
+            float c = 0.0f;
+            if (scale > 0.0f) {
+                c = __builtin_rintf(x[e] / scale);
+                c = fminf(fmaxf(c, -127.0f), 127.0f);
+            }
+            code[e] = (uint8_t)(int8_t)(int)c;
         }
-        code[e] = (int8_t)(int)c;
     }
 }
 
@@ -115,9 +149,10 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void store_int8_kernel(StoreArgs a) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void store_q8_kernel(StoreArgs a) {
     constexpr int EPL = D / 64;
+    constexpr float kMax = FP8 ? 448.0f : 127.0f;   // largest code magnitude
     const int32_t lane = threadIdx.x & 63;
     const int32_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int32_t h = blockIdx.y;
@@ -137,15 +172,15 @@ __global__ __launch_bounds__(256) void store_int8_kernel(StoreArgs a) {
     if (!locate(a, t, h, lane, ph, slot)) return;
     kmax = wave_max(kmax);
     vmax = wave_max(vmax);
-    const float ks = kmax / 127.0f;   // IEEE division (no fast-math in this build)
-    const float vs = vmax / 127.0f;
-    int8_t kc[EPL], vc[EPL];
-    encode<EPL>(kx, ks, kc);
-    encode<EPL>(vx, vs, vc);
-    int8_t* kdst = reinterpret_cast<int8_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
+    const float ks = kmax / kMax;   // IEEE division (no fast-math in this build)
+    const float vs = vmax / kMax;
+    uint8_t kc[EPL], vc[EPL];
+    encode<EPL, FP8>(kx, ks, kc);
+    encode<EPL, FP8>(vx, vs, vc);
+    uint8_t* kdst = reinterpret_cast<uint8_t*>(a.k_slab) + (ph * kPage + slot) * D + lane * EPL;
     if constexpr (EPL == 8) *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kc);
     else *reinterpret_cast<uint32_t*>(kdst) = *reinterpret_cast<uint32_t*>(kc);
-    int8_t* vdst = reinterpret_cast<int8_t*>(a.v_slab) + ph * kPage * D + slot;
+    uint8_t* vdst = reinterpret_cast<uint8_t*>(a.v_slab) + ph * kPage * D + slot;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) vdst[(lane * EPL + e) * kPage] = vc[e];
     if (lane == 0) {
@@ -180,9 +215,12 @@ int launch_store(const StoreLaunch& s, void* stream) {
     if (s.kv_dtype == PAKV_KV_BF16) {
         if (s.head_dim == 256) launch(K, store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
         else launch(K, store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
+    } else if (s.kv_dtype == PAKV_KV_FP8_PTH) {
+        if (s.head_dim == 256) launch(K, store_q8_kernel<256, true>, grid, dim3(256), 0, st, a);
+        else launch(K, store_q8_kernel<512, true>, grid, dim3(256), 0, st, a);
     } else {
-        if (s.head_dim == 256) launch(K, store_int8_kernel<256>, grid, dim3(256), 0, st, a);
-        else launch(K, store_int8_kernel<512>, grid, dim3(256), 0, st, a);
+        if (s.head_dim == 256) launch(K, store_q8_kernel<256, false>, grid, dim3(256), 0, st, a);
+        else launch(K, store_q8_kernel<512, false>, grid, dim3(256), 0, st, a);
     }
     return (int)hipGetLastError();
 }

@@ -146,8 +146,13 @@ pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_
             return fail(PAKV_ERR_UNSUPPORTED, "layer %d: group size %d above 16", l,
                         d.num_q_heads / d.num_kv_heads);
         if (d.window < 0) return fail(PAKV_ERR_INVALID, "layer %d: negative window", l);
-        if (d.kv_dtype != PAKV_KV_BF16 && d.kv_dtype != PAKV_KV_INT8_PTH)
+        if (d.kv_dtype != PAKV_KV_BF16 && d.kv_dtype != PAKV_KV_INT8_PTH && d.kv_dtype != PAKV_KV_FP8_PTH)
             return fail(PAKV_ERR_INVALID, "layer %d: unknown kv_dtype %d", l, d.kv_dtype);
+        if (d.k_eq_v != 0 && d.k_eq_v != 1) return fail(PAKV_ERR_INVALID, "layer %d: k_eq_v must be 0 or 1", l);
+        if (d.k_eq_v && !(d.v_norm_eps >= 0.0f && d.v_norm_eps < 1e30f))
+            return fail(PAKV_ERR_INVALID, "layer %d: v_norm_eps must be finite and not negative", l);
+        if (d.k_eq_v && d.kv_dtype != PAKV_KV_BF16)
+            return fail(PAKV_ERR_UNSUPPORTED, "layer %d: K=V storage is built for bf16 layers only", l);
         if (!(d.sm_scale > 0.0f) || d.sm_scale != d.sm_scale || d.sm_scale > 1e30f)
             return fail(PAKV_ERR_INVALID, "layer %d: sm_scale must be positive and finite", l);
         if (d.kv_source != -1) {
@@ -158,10 +163,11 @@ pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_
             if (sd.kv_source != -1)
                 return fail(PAKV_ERR_ALIAS, "layer %d: kv_source %d is itself KV-shared", l, s);
             if (sd.head_dim != d.head_dim || sd.num_kv_heads != d.num_kv_heads ||
-                sd.window != d.window || sd.kv_dtype != d.kv_dtype)
+                sd.window != d.window || sd.kv_dtype != d.kv_dtype || sd.k_eq_v != d.k_eq_v ||
+                (d.k_eq_v && sd.v_norm_eps != d.v_norm_eps))
                 return fail(PAKV_ERR_ALIAS,
-                            "layer %d: kv_source %d differs in head_dim, num_kv_heads, window or kv_dtype",
-                            l, s);
+                            "layer %d: kv_source %d differs in head_dim, num_kv_heads, window, kv_dtype or "
+                            "K=V storage", l, s);
         }
     }
     pakv_layer_map* m = new (std::nothrow) pakv_layer_map;
@@ -189,9 +195,9 @@ pakv_status pakv_layer_map_bind_slab(pakv_layer_map* map, int32_t layer, const p
     if (slab->page_size != PAKV_PAGE_SIZE)
         return fail(PAKV_ERR_UNSUPPORTED, "page_size %d (16 supported)", slab->page_size);
     if (slab->num_pages <= 0) return fail(PAKV_ERR_INVALID, "num_pages must be positive");
-    if (!slab->k || !slab->v) return fail(PAKV_ERR_INVALID, "slab k or v is null");
-    if (L.desc.kv_dtype == PAKV_KV_INT8_PTH && (!slab->k_scale || !slab->v_scale))
-        return fail(PAKV_ERR_INVALID, "int8 slab needs k_scale and v_scale");
+    if (!slab->k || (!slab->v && !L.desc.k_eq_v)) return fail(PAKV_ERR_INVALID, "slab k or v is null");
+    if (L.desc.kv_dtype != PAKV_KV_BF16 && (!slab->k_scale || !slab->v_scale))
+        return fail(PAKV_ERR_INVALID, "an 8-bit slab needs k_scale and v_scale");
     L.slab = *slab;
     L.bound = true;
     return PAKV_OK;
@@ -213,7 +219,7 @@ pakv_status pakv_kv_bytes_per_token(const pakv_layer_map* map, int64_t* full_byt
         if (L.source != (int32_t)l) continue;
         const pakv_layer_desc& d = L.desc;
         int64_t row = d.kv_dtype == PAKV_KV_BF16 ? 2 * (int64_t)d.head_dim : (int64_t)d.head_dim + 4;
-        int64_t bytes = (int64_t)d.num_kv_heads * 2 * row;
+        int64_t bytes = (int64_t)d.num_kv_heads * (d.k_eq_v ? 1 : 2) * row;
         if (d.window == 0) f += bytes; else w += bytes;
     }
     *full_bytes = f;
@@ -267,7 +273,7 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
     if (num_seqs < 0 || total_tokens < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
     if (pakv_status s = check_pages(pages, num_seqs)) return s;
     if (!cu_tokens || !start_pos) return fail(PAKV_ERR_INVALID, "cu_tokens or start_pos is null");
-    if (total_tokens > 0 && (!k || !v)) return fail(PAKV_ERR_INVALID, "k or v is null");
+    if (total_tokens > 0 && (!k || (!v && !L.desc.k_eq_v))) return fail(PAKV_ERR_INVALID, "k or v is null");
     if (!L.bound) return fail(PAKV_ERR_INVALID, "layer %d has no slab bound", layer);
     if (total_tokens == 0 || num_seqs == 0) return PAKV_OK;
     StoreLaunch a;
@@ -277,7 +283,7 @@ pakv_status pakv_paged_kv_store(const pakv_layer_map* map, int32_t layer, const 
     a.cu_tokens = cu_tokens;
     a.start_pos = start_pos;
     a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
+    a.v = L.desc.k_eq_v ? nullptr : static_cast<const uint16_t*>(v);
     a.num_seqs = num_seqs;
     a.total_tokens = total_tokens;
     a.hkv = L.desc.num_kv_heads;
@@ -327,6 +333,8 @@ static pakv_status decode_setup(const pakv_layer_map* map, int32_t layer, const 
     a.head_dim = L.desc.head_dim;
     a.window = L.desc.window;
     a.kv_dtype = L.desc.kv_dtype;
+    a.k_eq_v = S.desc.k_eq_v;
+    a.v_norm_eps = S.desc.v_norm_eps;
     a.sm_scale = L.desc.sm_scale;
     a.plan = plan_decode(L.desc, num_seqs);
     a.layout = plan_layout(num_seqs, a.hkv, max_kv_len);
@@ -399,8 +407,9 @@ pakv_status pakv_paged_attn_decode_append(const pakv_layer_map* map, int32_t lay
     if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
     const auto& L = map->layers[layer];
     const bool owner = L.source == layer;
-    if (owner && L.desc.kv_dtype != PAKV_KV_BF16)
-        return fail(PAKV_ERR_UNSUPPORTED, "append decode on an int8 layer is not built: store, then decode");
+    if (owner && (L.desc.kv_dtype != PAKV_KV_BF16 || L.desc.k_eq_v))
+        return fail(PAKV_ERR_UNSUPPORTED,
+                    "append decode on an 8-bit or K=V layer is not built: store, then decode");
     if (owner && num_seqs > 0 && (!k_new || !v_new)) return fail(PAKV_ERR_INVALID, "k_new or v_new is null");
     DecodeLaunch a;
     if (pakv_status s = decode_setup(map, layer, pages, num_seqs, max_kv_len, a)) return s;
@@ -478,12 +487,13 @@ pakv_status pakv_paged_attn_decode_noalloc(const pakv_layer_map* map, int32_t la
 
 size_t pakv_decode_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
 
-pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
-                                   const int32_t* cu_q, const int32_t* prefix_lens,
-                                   const void* q, void* out,
-                                   int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                                   int32_t max_kv_len, void* stream) {
-    clear_error();
+// Checks shared by the extend calls; k_ext / v_ext: the packed chunk rows (or
+// null: the chunk is read from the slab).
+static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                               const int32_t* cu_q, const int32_t* prefix_lens, const void* q,
+                               const void* k_ext, const void* v_ext, void* out,
+                               int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                               bool packed, void* stream) {
     if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
     if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PAKV_OK;
@@ -494,12 +504,14 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
                     pages->max_pages_per_seq * PAKV_PAGE_SIZE);
     if (!cu_q || !prefix_lens || !q || !out) return fail(PAKV_ERR_INVALID, "null pointer argument");
     const auto& L = map->layers[layer];
-    if (L.desc.kv_dtype != PAKV_KV_BF16)
-        return fail(PAKV_ERR_UNSUPPORTED, "extend on an int8 layer is not built");
     const auto& S = map->layers[L.source];
+    if (packed && (!k_ext || (!v_ext && !S.desc.k_eq_v)))
+        return fail(PAKV_ERR_INVALID, "k_ext or v_ext is null");
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
-    // grid (Hkv, row blocks of 128 (token, head) rows, sequences)
-    const int64_t row_blocks = ((int64_t)max_q_len * (L.desc.num_q_heads / L.desc.num_kv_heads) + 127) / 128;
+    const int32_t group = L.desc.num_q_heads / L.desc.num_kv_heads;
+    const bool fast = L.desc.kv_dtype == PAKV_KV_BF16 && !S.desc.k_eq_v && !packed;
+    // grid (Hkv, row blocks of 128 (fast) or 32 (general) (token, head) rows, sequences)
+    const int64_t row_blocks = ((int64_t)max_q_len * group + (fast ? 127 : 31)) / (fast ? 128 : 32);
     if (row_blocks > 65535 || num_seqs > 65535)
         return fail(PAKV_ERR_UNSUPPORTED, "extend grid too large: %lld row blocks, %d sequences (65535 each at most)",
                     (long long)row_blocks, num_seqs);
@@ -510,6 +522,8 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
     a.cu_q = cu_q;
     a.prefix_lens = prefix_lens;
     a.q = static_cast<const uint16_t*>(q);
+    a.k_ext = packed ? static_cast<const uint16_t*>(k_ext) : nullptr;
+    a.v_ext = packed && !S.desc.k_eq_v ? static_cast<const uint16_t*>(v_ext) : nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.num_seqs = num_seqs;
     a.total_q = total_q;
@@ -520,7 +534,31 @@ pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, con
     a.head_dim = L.desc.head_dim;
     a.window = L.desc.window;
     a.sm_scale = L.desc.sm_scale;
-    return hip_status(launch_extend(a, stream), "paged_attn_extend launch");
+    a.kv_dtype = L.desc.kv_dtype;
+    a.k_eq_v = S.desc.k_eq_v;
+    a.v_norm_eps = S.desc.v_norm_eps;
+    if (fast) return hip_status(launch_extend(a, stream), "paged_attn_extend launch");
+    return hip_status(launch_extend_general(a, stream), "paged_attn_extend launch");
+}
+
+pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                   const int32_t* cu_q, const int32_t* prefix_lens,
+                                   const void* q, void* out,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                   int32_t max_kv_len, void* stream) {
+    clear_error();
+    return extend_call(map, layer, pages, cu_q, prefix_lens, q, nullptr, nullptr, out, num_seqs, total_q, max_q_len,
+                       max_kv_len, false, stream);
+}
+
+pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const int32_t* cu_q, const int32_t* prefix_lens,
+                                          const void* q, const void* k_ext, const void* v_ext, void* out,
+                                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, void* stream) {
+    clear_error();
+    return extend_call(map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q, max_q_len,
+                       max_kv_len, true, stream);
 }
 
 pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream) {

@@ -87,7 +87,7 @@ struct StoreLaunch {
     const int32_t* cu_tokens;
     const int32_t* start_pos;
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* v;      // null for a K=V layer
     int32_t num_seqs;
     int32_t total_tokens;
     int32_t hkv;
@@ -110,6 +110,8 @@ struct DecodeLaunch {
     int32_t head_dim;
     int32_t window;
     int32_t kv_dtype;
+    int32_t k_eq_v;         // values are the RMS-normalised keys (K slab only)
+    float v_norm_eps;
     float sm_scale;
     DecodePlan plan;
     int32_t* sched;     // the schedule buffer (written by the plan kernel, read by the decode kernel)
@@ -142,6 +144,8 @@ struct ExtendLaunch {
     const int32_t* cu_q;
     const int32_t* prefix_lens;
     const uint16_t* q;
+    const uint16_t* k_ext = nullptr;   // packed chunk rows [total_q][Hkv][D], or null (chunk read from the slab)
+    const uint16_t* v_ext = nullptr;
     uint16_t* out;
     int32_t num_seqs;
     int32_t total_q;
@@ -152,8 +156,12 @@ struct ExtendLaunch {
     int32_t head_dim;
     int32_t window;
     float sm_scale;
+    int32_t kv_dtype = PAKV_KV_BF16;
+    int32_t k_eq_v = 0;
+    float v_norm_eps = 0.f;
 };
-int launch_extend(const ExtendLaunch& a, void* stream);
+int launch_extend(const ExtendLaunch& a, void* stream);           // bf16 K and V slabs, chunk in the slab
+int launch_extend_general(const ExtendLaunch& a, void* stream);   // 8-bit, K=V, packed chunks
 
 const char* hip_error_string(int err);
 

@@ -23,7 +23,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(6)
-KV_BF16, KV_INT8_PTH = 0, 1
+KV_BF16, KV_INT8_PTH, KV_FP8_PTH = 0, 1, 2
 PAGE_SIZE = 16
 
 EXPORTED = (
@@ -33,7 +33,7 @@ EXPORTED = (
     "pakv_decode_plan_bytes", "pakv_decode_plan", "pakv_paged_attn_decode_planned",
     "pakv_paged_attn_decode_append",
     "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used", "pakv_workgroup_xcds",
-    "pakv_paged_attn_decode_noalloc", "pakv_decode_noalloc_max_bytes",
+    "pakv_paged_attn_decode_noalloc", "pakv_decode_noalloc_max_bytes", "pakv_paged_attn_extend_packed",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -44,7 +44,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("kv_source", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("k_eq_v", ctypes.c_int32),
+                ("v_norm_eps", ctypes.c_float)]
 
 
 class Slab(ctypes.Structure):
@@ -99,6 +100,9 @@ lib.pakv_decode_noalloc_max_bytes.restype = _S
 lib.pakv_decode_noalloc_max_bytes.argtypes = []
 lib.pakv_paged_attn_extend.restype = _I
 lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _I, _I, _I, _I, _P]
+lib.pakv_paged_attn_extend_packed.restype = _I
+lib.pakv_paged_attn_extend_packed.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                              _P]
 lib.pakv_set_timing_events.restype = _I
 lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
 lib.pakv_timing_pairs_used.restype = _I
@@ -254,6 +258,13 @@ def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_se
     return _check(lib.pakv_paged_attn_extend(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                              _ptr(prefix_lens), _ptr(q), _ptr(out), num_seqs, total_q,
                                              max_q_len, max_kv_len, _stream(stream)))
+
+
+def paged_attn_extend_packed(layer_map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q,
+                             max_q_len, max_kv_len, stream=None):
+    return _check(lib.pakv_paged_attn_extend_packed(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
+                                                    _ptr(prefix_lens), _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(out),
+                                                    num_seqs, total_q, max_q_len, max_kv_len, _stream(stream)))
 
 
 def workgroup_xcds(out, num_workgroups, stream=None):

@@ -40,17 +40,23 @@
  *   V codes : [num_pages][Hkv][D][16]  dim-major inside a page (each dim's 16
  *             tokens are contiguous), so that the value contraction over tokens
  *             reads contiguous runs
- *   codes are bf16 (2 bytes) for PAKV_KV_BF16 and int8 for PAKV_KV_INT8_PTH.
- *   int8 scales: k_scale, v_scale : float32 [num_pages][Hkv][16], one per token
- *   and KV head (FreeToken PR #898, description bullet on the per-token-head
- *   formats; "End to end": D + 4 bytes per row).
+ *   codes are bf16 (2 bytes) for PAKV_KV_BF16, int8 for PAKV_KV_INT8_PTH and
+ *   OCP FP8 E4M3 bytes for PAKV_KV_FP8_PTH.
+ *   8-bit scales: k_scale, v_scale : float32 [num_pages][Hkv][16], one per
+ *   token and KV head (FreeToken PR #898, description bullet on the
+ *   per-token-head formats; "End to end": D + 4 bytes per row for either
+ *   8-bit format).
+ *   A K=V layer (k_eq_v below) has a K slab only: its values are derived from
+ *   the stored keys whenever they are read.
  * Every (page, head) block is 16*D codes, contiguous.
  *
- * int8 per-token-head encoding (the pages do not print it; this library's
- * reading): for a row x of D bf16 values, amax = max|x_d|, scale =
- * fl32(amax / 127) by IEEE float32 division, code_d = clamp(rne(fl32(x_d /
- * scale)), -127, 127); an all-zero row gets scale 0 and zero codes.  A stored
- * element decodes to code * scale.
+ * 8-bit per-token-head encodings (the pages do not print them; this library's
+ * reading): for a row x of D bf16 values, amax = max|x_d| and scale =
+ * fl32(amax / M) by IEEE float32 division, M = 127 (int8) or 448 (fp8, the
+ * largest E4M3 value); y_d = fl32(x_d / scale); int8: code_d =
+ * clamp(rne(y_d), -127, 127); fp8: code_d = the E4M3 value nearest y_d, ties
+ * to the even mantissa, saturating at +-448.  An all-zero row gets scale 0
+ * and zero codes.  A stored element decodes to value(code) * scale.
  */
 #ifndef PAKV_H
 #define PAKV_H
@@ -75,7 +81,8 @@ typedef enum {
 
 typedef enum {
     PAKV_KV_BF16 = 0,     /* bf16 codes */
-    PAKV_KV_INT8_PTH = 1  /* int8 codes + one float32 scale per token and KV head */
+    PAKV_KV_INT8_PTH = 1, /* int8 codes + one float32 scale per token and KV head */
+    PAKV_KV_FP8_PTH = 2   /* fp8 E4M3 codes + one float32 scale per token and KV head */
 } pakv_kv_dtype;
 
 /* Per-layer description.
@@ -88,7 +95,16 @@ typedef enum {
  *   kv_source     : -1 if the layer owns a slab, else the index of the owning
  *                   layer whose slab it reads.
  *   kv_dtype      : a pakv_kv_dtype.
- *   sm_scale      : softmax scale applied to q.k (for example 1/sqrt(head_dim)). */
+ *   sm_scale      : softmax scale applied to q.k (for example 1/sqrt(head_dim)).
+ *   k_eq_v        : 1 for a layer whose value row is its key row RMS-normalised
+ *                   without a learned scale, v = k / sqrt(mean_d k_d^2 +
+ *                   v_norm_eps) (unsloth commit 749fb75: attention_k_eq_v on
+ *                   the full layers, the value being the key projection
+ *                   followed only by a scale-free v_norm; pegainfer issue #807,
+ *                   Description, third paragraph: whether K and V can share
+ *                   storage).  Such a layer stores and reads its K slab only;
+ *                   bf16 layers only in this build.  0 otherwise.
+ *   v_norm_eps    : the eps of that norm (k_eq_v layers; e.g. 1e-6). */
 typedef struct {
     int32_t head_dim;
     int32_t num_q_heads;
@@ -97,10 +113,12 @@ typedef struct {
     int32_t kv_source;
     int32_t kv_dtype;
     float sm_scale;
+    int32_t k_eq_v;
+    float v_norm_eps;
 } pakv_layer_desc;
 
 /* Device buffers of one owning layer's slab (layout above).  k_scale / v_scale
- * are NULL for bf16 slabs.  page_size must be 16. */
+ * are NULL for bf16 slabs; v is NULL for a K=V layer.  page_size must be 16. */
 typedef struct {
     void* k;
     void* v;
@@ -137,9 +155,10 @@ pakv_status pakv_resolve_kv_sources(int32_t n_layers, const int32_t* layer_type,
 
 /* Builds the host-side map of n layers from descs (copied; host memory).
  * Returns PAKV_ERR_ALIAS if some kv_source is not an earlier layer, is itself
- * shared, or differs from the layer in head_dim, num_kv_heads, window or
- * kv_dtype; PAKV_ERR_UNSUPPORTED for a head_dim other than 256 / 512 or a
- * group size Hq / Hkv above 16; PAKV_ERR_INVALID for other bad fields.
+ * shared, or differs from the layer in head_dim, num_kv_heads, window,
+ * kv_dtype, k_eq_v or v_norm_eps; PAKV_ERR_UNSUPPORTED for a head_dim other
+ * than 256 / 512, a group size Hq / Hkv above 16 or an 8-bit K=V layer;
+ * PAKV_ERR_INVALID for other bad fields.
  * On success *out owns the map; release it with pakv_layer_map_destroy. */
 pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_layer_map** out);
 void pakv_layer_map_destroy(pakv_layer_map* map);
@@ -154,8 +173,9 @@ pakv_status pakv_layer_map_source(const pakv_layer_map* map, int32_t layer, int3
 
 /* KV bytes per token over owning layers only (FreeToken PR #898, description,
  * third bullet: only layers that own KV are priced), split into the full group
- * (window == 0) and the window group: sum of Hkv * 2 * row, row = 2*D for bf16
- * and D + 4 for int8 per-token-head. */
+ * (window == 0) and the window group: sum of Hkv * 2 * row (Hkv * row for a
+ * K=V layer, which stores no V), row = 2*D for bf16 and D + 4 for the 8-bit
+ * per-token-head formats. */
 pakv_status pakv_kv_bytes_per_token(const pakv_layer_map* map, int64_t* full_bytes, int64_t* window_bytes);
 
 /* Bytes of the K (or V) code buffer and of one scale buffer for a slab of
@@ -168,8 +188,9 @@ pakv_status pakv_slab_bytes(const pakv_layer_map* map, int32_t layer, int32_t nu
  *                 cu_tokens[b] .. cu_tokens[b+1]-1 of k and v
  *   start_pos   : device int32 [num_seqs]; row i of sequence b goes to position
  *                 start_pos[b] + i
- *   k, v        : device bf16 [total_tokens][Hkv][D], token-major
- * For an int8 layer the rows are encoded in-kernel (see the header comment).
+ *   k, v        : device bf16 [total_tokens][Hkv][D], token-major (v is not
+ *                 read, and may be NULL, for a K=V layer)
+ * For an 8-bit layer the rows are encoded in-kernel (see the header comment).
  * A shared layer returns PAKV_OK and launches nothing: its source stored the
  * same rows earlier in the forward (FreeToken PR #898, description, fourth
  * bullet).  Rows whose position falls outside the page table are dropped. */
@@ -261,8 +282,8 @@ pakv_status pakv_paged_attn_decode_planned(const pakv_layer_map* map, int32_t la
  * lies outside [0, num_pages) is not written, as pakv_paged_kv_store drops
  * such rows; the new token is still attended.  A shared layer stores nothing (its source's call stored
  * the row) and k_new/v_new may be NULL: the call is then a planned decode.  An
- * owning layer with int8 K/V returns PAKV_ERR_UNSUPPORTED before any launch
- * (call pakv_paged_kv_store, then the planned decode). */
+ * owning layer with 8-bit or K=V storage returns PAKV_ERR_UNSUPPORTED before
+ * any launch (call pakv_paged_kv_store, then the planned decode). */
 pakv_status pakv_paged_attn_decode_append(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                           const void* plan, size_t plan_bytes, const void* k_new,
                                           const void* v_new, const void* q, void* out,
@@ -295,13 +316,32 @@ size_t pakv_decode_noalloc_max_bytes(void);
  *                 prefix_lens[b] + n_b
  * The chunk's own K/V must already be stored (by the source for a shared layer,
  * as the source runs earlier in the forward); the kernel reads prefix and chunk
- * from the slab.  bf16 layers only in this build (PAKV_ERR_UNSUPPORTED for
- * int8). */
+ * from the slab.  Every format: bf16 slabs go to an extend kernel built for
+ * them; 8-bit and K=V layers to one that stages each tile in bf16 (exact
+ * codes, scales applied to the scores and the weights). */
 pakv_status pakv_paged_attn_extend(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                    const int32_t* cu_q, const int32_t* prefix_lens,
                                    const void* q, void* out,
                                    int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                    int32_t max_kv_len, void* stream);
+
+/* Chunked prefill with the chunk's own keys and values given as packed rows
+ * (FreeToken PR #898, description, fourth bullet: the extend kernel takes the
+ * current chunk from k_extend / v_extend, and the attention module passes k, v
+ * to the backend even on a shared layer): positions prefix_lens[b] ..
+ * prefix_lens[b] + n_b - 1 read k_ext / v_ext, exactly as given in bf16
+ * whatever format the slab stores; only the prefix (positions below
+ * prefix_lens[b]) is read from the slab.  The call stores nothing: an owning
+ * layer's pakv_paged_kv_store of the same rows may come before or after it.
+ *   k_ext, v_ext : device bf16 [total_q][Hkv][D], token-major, packed by cu_q
+ *                  (for a shared layer, its source's rows); v_ext is not read,
+ *                  and may be NULL, for a K=V layer (values from k_ext)
+ * Other arguments as in pakv_paged_attn_extend. */
+pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const int32_t* cu_q, const int32_t* prefix_lens,
+                                          const void* q, const void* k_ext, const void* v_ext, void* out,
+                                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, void* stream);
 
 /* Placement check.  Launches num_workgroups (1 .. 65535) workgroups on
  * stream; workgroup i writes the id of the XCD it ran on to out[i] (device

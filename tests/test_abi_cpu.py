@@ -45,7 +45,7 @@ def _model(name, fmt, share):
     hkv = 1 if name == "E2B" else 2
     tags = [1 if t == "full" else 0 for t in types]
     src = pakv.resolve_kv_sources(tags, first if share else len(types))
-    dtype = pakv.KV_BF16 if fmt == "bf16" else pakv.KV_INT8_PTH
+    dtype = {"bf16": pakv.KV_BF16, "int8": pakv.KV_INT8_PTH, "fp8": pakv.KV_FP8_PTH}[fmt]
     descs = []
     for l, t in enumerate(types):
         d, w = (512, 0) if t == "full" else (256, 512)
@@ -159,9 +159,11 @@ def test_argument_errors_are_returned_before_launch():
     # decode: no sequences -> nothing to do
     assert lib.pakv_paged_attn_decode(m.handle, 0, ctypes.byref(pages), None, None, None, 0, 40,
                                       None, 0, None) == pakv.OK
-    # extend on an int8 layer is not built
-    assert lib.pakv_paged_attn_extend(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x7000,
-                                      2, 10, 5, 40, None) == pakv.ERR_UNSUPPORTED
+    # packed extend without its key rows (or values, on a layer that stores V)
+    assert lib.pakv_paged_attn_extend_packed(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, None,
+                                             0x6300, 0x7000, 2, 10, 5, 40, None) == pakv.ERR_INVALID
+    assert lib.pakv_paged_attn_extend_packed(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x6300,
+                                             None, 0x7000, 2, 10, 5, 40, None) == pakv.ERR_INVALID
     # extend: empty chunk -> nothing to do
     assert lib.pakv_paged_attn_extend(m.handle, 0, ctypes.byref(pages), None, None, None, None,
                                       2, 0, 0, 40, None) == pakv.OK
@@ -290,3 +292,40 @@ def test_noalloc_decode_refuses_what_its_scratch_cannot_hold():
                                               None) == pakv.ERR_INVALID
     assert lib.pakv_paged_attn_decode_noalloc(m.handle, 0, ctypes.byref(pages), None, None, None, 0, 40,
                                               None) == pakv.OK
+
+
+def test_k_eq_v_layers_store_keys_only():
+    """A K=V layer binds no V buffer, prices one row per token and head, may
+    only be read by shared layers of the same kind, and is built for bf16."""
+    eps = 1e-6
+    kv = lambda src=-1, dtype=pakv.KV_BF16, e=eps: pakv.LayerDesc(512, 16, 2, 0, src, dtype, 0.044, 1, e)
+    m = pakv.LayerMap([kv(), kv(src=0)])
+    m.bind_slab(0, 0x1000, None, 8)
+    assert m.kv_bytes_per_token() == (2 * 1 * 1024, 0)
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap([kv(), pakv.LayerDesc(512, 16, 2, 0, 0, pakv.KV_BF16, 0.044)])    # source stores K only
+    assert e.value.status == pakv.ERR_ALIAS
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap([kv(), kv(src=0, e=1e-5)])
+    assert e.value.status == pakv.ERR_ALIAS
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap([kv(dtype=pakv.KV_INT8_PTH)])
+    assert e.value.status == pakv.ERR_UNSUPPORTED
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap([kv(e=-1.0)])
+    assert e.value.status == pakv.ERR_INVALID
+    # a layer that stores V still needs its V buffer
+    m2 = pakv.LayerMap([_desc()])
+    with pytest.raises(pakv.PakvError):
+        m2.bind_slab(0, 0x1000, None, 8)
+
+
+def test_fp8_layers_need_scales_and_share_only_with_fp8():
+    m = pakv.LayerMap([_desc(dtype=pakv.KV_FP8_PTH)])
+    with pytest.raises(pakv.PakvError):
+        m.bind_slab(0, 0x1000, 0x2000, 8)
+    m.bind_slab(0, 0x1000, 0x2000, 8, 0x3000, 0x4000)
+    assert m.kv_bytes_per_token() == (2 * (256 + 4), 0)
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.LayerMap([_desc(dtype=pakv.KV_FP8_PTH), _desc(src=0, dtype=pakv.KV_INT8_PTH)])
+    assert e.value.status == pakv.ERR_ALIAS

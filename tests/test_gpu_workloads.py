@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, quantise_rows, dequantise_rows
+from oracle import attend, quantise_rows, dequantise_rows, v_from_k
+from workloads.configs import V_NORM_EPS
 from workloads import (DeviceDraws, bf16_to_f32, e2b_decode_workload, e2b_extend_workload,
                        int8_long_workload, make_page_pool, moe26b_decode_workload, tiny_workload)
 
@@ -74,10 +75,14 @@ class DeviceScenario:
         """(positions, k, v) float64 of the slab `layer` reads, as the oracle
         sees it (int8 layers: the oracle's own encoding of the drawn rows)."""
         pos, k, v = self.kept[(self.cache.sources[layer], b)]
-        if self.wl.layers[layer].kv_dtype == "int8":
+        spec = self.wl.layers[layer]
+        if spec.kv_dtype == "int8":
             kq, ks = quantise_rows(k)
             vq, vs = quantise_rows(v)
-            return pos, dequantise_rows(kq, ks), dequantise_rows(vq, vs)
+            k, v = dequantise_rows(kq, ks), dequantise_rows(vq, vs)
+        if spec.k_eq_v and self.cache.specs[layer]["k_eq_v"]:
+            # one slab: the library derives the values from the stored keys
+            return pos, k.astype(np.float64), v_from_k(k, V_NORM_EPS)
         return pos, k.astype(np.float64), v.astype(np.float64)
 
 

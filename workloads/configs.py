@@ -14,6 +14,11 @@ from typing import List, Optional
 import numpy as np
 
 
+# eps of the value norm of K=V layers (Gemma's RMS norms use 1e-6; the pages
+# do not print it)
+V_NORM_EPS = 1e-6
+
+
 @dataclass
 class LayerSpec:
     type: str            # "full" or "sliding"
@@ -21,7 +26,7 @@ class LayerSpec:
     num_q_heads: int
     num_kv_heads: int
     window: int          # 0 for full layers
-    kv_dtype: str = "bf16"   # "bf16" or "int8"
+    kv_dtype: str = "bf16"   # "bf16", "int8" or "fp8"
     k_eq_v: bool = False     # value rows are the RMS-normalised key rows
 
     @property
@@ -31,7 +36,8 @@ class LayerSpec:
     def as_dict(self):
         return dict(type=self.type, head_dim=self.head_dim, num_q_heads=self.num_q_heads,
                     num_kv_heads=self.num_kv_heads, window=self.window,
-                    kv_dtype=self.kv_dtype, sm_scale=self.sm_scale)
+                    kv_dtype=self.kv_dtype, sm_scale=self.sm_scale, k_eq_v=self.k_eq_v,
+                    v_norm_eps=V_NORM_EPS)
 
 
 @dataclass
