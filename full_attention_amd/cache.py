@@ -47,6 +47,8 @@ class PagedKVCache:
                                         self.DTYPES[s["kv_dtype"]], float(s["sm_scale"]),
                                         1 if s["k_eq_v"] else 0, s["v_norm_eps"]))
         self.map = pakv.LayerMap(descs)
+        # num_pages: one pool size for every slab, or {"sliding": n, "full": m}
+        # when each group has its own pool (a window pool for the sliding group)
         self.num_pages = num_pages
         self.device = torch.device(device)
         self.slabs = {}
@@ -54,38 +56,62 @@ class PagedKVCache:
             if self.sources[l] != l:
                 continue
             hkv, d = s["num_kv_heads"], s["head_dim"]
-            if s["kv_dtype"] == "bf16":
-                fill = 0x7FC0 if sentinel else 0            # bf16 quiet NaN
-                k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int16, device=self.device)
-                v = None if s["k_eq_v"] else torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int16,
-                                                        device=self.device)
-                ks = vs = None
+            if isinstance(num_pages, dict):
+                num_pages_l = num_pages["sliding" if s["window"] > 0 else "full"]
             else:
-                # int8: -128, a code the encoder never makes; fp8: 0xFF, an E4M3 NaN
-                fill = (-128 if s["kv_dtype"] == "int8" else -1) if sentinel else 0
-                k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int8, device=self.device)
-                v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int8, device=self.device)
-                sfill = float("nan") if sentinel else 0.0
-                ks = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
-                vs = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
-            self.map.bind_slab(l, k, v, num_pages, ks, vs)
-            self.slabs[l] = (k, v, ks, vs)
+                num_pages_l = num_pages
+            self._fill_slab(l, s, hkv, d, num_pages_l, sentinel)
         self.pages = None
         self.page_table = None
+        self._group_pages = {}     # "sliding" / "full" -> (table tensor, pakv_pages) of that group
         self._workspace = None
+
+    def _fill_slab(self, l, s, hkv, d, num_pages, sentinel):
+        """Allocates and binds owner layer l's slab, filled with a sentinel
+        (a NaN, or a code the encoders never make) where nothing is stored."""
+        if s["kv_dtype"] == "bf16":
+            fill = 0x7FC0 if sentinel else 0            # bf16 quiet NaN
+            k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int16, device=self.device)
+            v = None if s["k_eq_v"] else torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int16,
+                                                    device=self.device)
+            ks = vs = None
+        else:
+            # int8: -128, a code the encoder never makes; fp8: 0xFF, an E4M3 NaN
+            fill = (-128 if s["kv_dtype"] == "int8" else -1) if sentinel else 0
+            k = torch.full((num_pages, hkv, 16, d), fill, dtype=torch.int8, device=self.device)
+            v = torch.full((num_pages, hkv, d, 16), fill, dtype=torch.int8, device=self.device)
+            sfill = float("nan") if sentinel else 0.0
+            ks = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
+            vs = torch.full((num_pages, hkv, 16), sfill, dtype=torch.float32, device=self.device)
+        self.map.bind_slab(l, k, v, num_pages, ks, vs)
+        self.slabs[l] = (k, v, ks, vs)
 
     def slab_of(self, layer):
         return self.slabs[self.sources[layer]]
 
-    def set_page_table(self, page_table):
-        """page_table: int32 [B, max_pages] (host or device)."""
-        self.page_table = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
-        self.pages = pakv.make_pages(self.page_table)
+    def set_page_table(self, page_table, group=None):
+        """page_table: int32 [B, max_pages] (host or device).  group None: one
+        table for every layer; "sliding" or "full": that group's own table (a
+        window pool's, for the sliding group), used by its layers in place of
+        the shared one."""
+        t = torch.as_tensor(page_table, dtype=torch.int32).to(self.device).contiguous()
+        if group is None:
+            self.page_table = t
+            self.pages = pakv.make_pages(self.page_table)
+        else:
+            assert group in ("sliding", "full")
+            self._group_pages[group] = (t, pakv.make_pages(t))
+
+    def pages_of(self, layer):
+        group = "sliding" if self.specs[layer]["window"] > 0 else "full"
+        if group in self._group_pages:
+            return self._group_pages[group][1]
+        return self.pages
 
     def store(self, layer, cu_tokens, start_pos, k, v=None, stream=None):
         total = k.shape[0]
         nseq = cu_tokens.shape[0] - 1
-        pakv.paged_kv_store(self.map, layer, self.pages, cu_tokens, start_pos, k, v, nseq, total, stream)
+        pakv.paged_kv_store(self.map, layer, self.pages_of(layer), cu_tokens, start_pos, k, v, nseq, total, stream)
 
     def workspace(self, layer, num_seqs, max_kv_len):
         need = pakv.decode_workspace_bytes(self.map, layer, num_seqs, max_kv_len)
@@ -118,7 +144,7 @@ class PagedKVCache:
         nseq = kv_lens.shape[0]
         nbytes = pakv.decode_plan_bytes(self.map, layer, nseq, max_kv_len)
         plan = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
-        pakv.decode_plan(self.map, layer, self.pages, kv_lens, nseq, max_kv_len, plan, plan.numel(), stream)
+        pakv.decode_plan(self.map, layer, self.pages_of(layer), kv_lens, nseq, max_kv_len, plan, plan.numel(), stream)
         return plan
 
     def decode(self, layer, kv_lens, q, max_kv_len, out=None, stream=None, plan=None):
@@ -129,10 +155,10 @@ class PagedKVCache:
             out = torch.empty_like(q)
         ws, need = self.workspace(layer, nseq, max_kv_len)
         if plan is None:
-            pakv.paged_attn_decode(self.map, layer, self.pages, kv_lens, q, out, nseq, max_kv_len,
+            pakv.paged_attn_decode(self.map, layer, self.pages_of(layer), kv_lens, q, out, nseq, max_kv_len,
                                    ws, ws.numel(), stream)
         else:
-            pakv.paged_attn_decode_planned(self.map, layer, self.pages, plan, plan.numel(), q, out, nseq,
+            pakv.paged_attn_decode_planned(self.map, layer, self.pages_of(layer), plan, plan.numel(), q, out, nseq,
                                            max_kv_len, ws, ws.numel(), stream)
         return out
 
@@ -144,7 +170,7 @@ class PagedKVCache:
         if out is None:
             out = torch.empty_like(q)
         ws, need = self.workspace(layer, nseq, max_kv_len)
-        pakv.paged_attn_decode_append(self.map, layer, self.pages, plan, plan.numel(), k_new, v_new, q, out, nseq,
+        pakv.paged_attn_decode_append(self.map, layer, self.pages_of(layer), plan, plan.numel(), k_new, v_new, q, out, nseq,
                                       max_kv_len, ws, ws.numel(), stream)
         return out
 
@@ -152,7 +178,7 @@ class PagedKVCache:
         nseq = cu_q.shape[0] - 1
         if out is None:
             out = torch.empty_like(q)
-        pakv.paged_attn_extend(self.map, layer, self.pages, cu_q, prefix_lens, q, out, nseq, q.shape[0],
+        pakv.paged_attn_extend(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, out, nseq, q.shape[0],
                                max_q_len, max_kv_len, stream)
         return out
 
@@ -163,6 +189,6 @@ class PagedKVCache:
         nseq = cu_q.shape[0] - 1
         if out is None:
             out = torch.empty_like(q)
-        pakv.paged_attn_extend_packed(self.map, layer, self.pages, cu_q, prefix_lens, q, k_ext, v_ext, out, nseq,
+        pakv.paged_attn_extend_packed(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, k_ext, v_ext, out, nseq,
                                       q.shape[0], max_q_len, max_kv_len, stream)
         return out

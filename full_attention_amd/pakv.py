@@ -34,6 +34,8 @@ EXPORTED = (
     "pakv_paged_attn_decode_append",
     "pakv_paged_attn_extend", "pakv_set_timing_events", "pakv_timing_pairs_used", "pakv_workgroup_xcds",
     "pakv_paged_attn_decode_noalloc", "pakv_decode_noalloc_max_bytes", "pakv_paged_attn_extend_packed",
+    "pakv_page_pool_create", "pakv_page_pool_destroy", "pakv_page_pool_reserve", "pakv_page_pool_release_seq",
+    "pakv_page_pool_table", "pakv_page_pool_free_pages", "pakv_page_pool_released", "pakv_pool_tokens",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -103,6 +105,23 @@ lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P
 lib.pakv_paged_attn_extend_packed.restype = _I
 lib.pakv_paged_attn_extend_packed.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                               _P]
+lib.pakv_page_pool_create.restype = _I
+lib.pakv_page_pool_create.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_P)]
+lib.pakv_page_pool_destroy.restype = None
+lib.pakv_page_pool_destroy.argtypes = [_P]
+lib.pakv_page_pool_reserve.restype = _I
+lib.pakv_page_pool_reserve.argtypes = [_P, _I, _I, _I]
+lib.pakv_page_pool_release_seq.restype = _I
+lib.pakv_page_pool_release_seq.argtypes = [_P, _I]
+lib.pakv_page_pool_table.restype = ctypes.POINTER(_I)
+lib.pakv_page_pool_table.argtypes = [_P]
+lib.pakv_page_pool_free_pages.restype = _I
+lib.pakv_page_pool_free_pages.argtypes = [_P]
+lib.pakv_page_pool_released.restype = _I
+lib.pakv_page_pool_released.argtypes = [_P, _P, _I]
+lib.pakv_pool_tokens.restype = _I
+lib.pakv_pool_tokens.argtypes = [_P, ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.POINTER(ctypes.c_int64)]
 lib.pakv_set_timing_events.restype = _I
 lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
 lib.pakv_timing_pairs_used.restype = _I
@@ -265,6 +284,57 @@ def paged_attn_extend_packed(layer_map, layer, pages, cu_q, prefix_lens, q, k_ex
     return _check(lib.pakv_paged_attn_extend_packed(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                                     _ptr(prefix_lens), _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(out),
                                                     num_seqs, total_q, max_q_len, max_kv_len, _stream(stream)))
+
+
+class PagePool:
+    """Owner of a pakv_page_pool* (host bookkeeping of which pages each
+    sequence holds, for one group of layers)."""
+
+    def __init__(self, num_pages, max_seqs, max_pages_per_seq, window):
+        handle = _P()
+        _check(lib.pakv_page_pool_create(num_pages, max_seqs, max_pages_per_seq, window, ctypes.byref(handle)))
+        self.handle = handle
+        self.shape = (max_seqs, max_pages_per_seq)
+
+    def close(self):
+        if self.handle:
+            lib.pakv_page_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reserve(self, seq, first_query, end):
+        _check(lib.pakv_page_pool_reserve(self.handle, seq, first_query, end))
+
+    def release_seq(self, seq):
+        _check(lib.pakv_page_pool_release_seq(self.handle, seq))
+
+    def table(self):
+        """A copy of the host table, int32 [max_seqs, max_pages_per_seq]."""
+        import numpy as np
+        p = lib.pakv_page_pool_table(self.handle)
+        n = self.shape[0] * self.shape[1]
+        return np.ctypeslib.as_array(p, shape=(n,)).reshape(self.shape).copy()
+
+    def free_pages(self):
+        return lib.pakv_page_pool_free_pages(self.handle)
+
+    def released(self):
+        n = lib.pakv_page_pool_released(self.handle, None, 0)
+        buf = (_I * max(n, 1))()
+        lib.pakv_page_pool_released(self.handle, ctypes.cast(buf, _P), n)
+        return list(buf)[:n]
+
+
+def pool_tokens(layer_map, budget_bytes, window_share):
+    f, w = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.pakv_pool_tokens(layer_map.handle, int(budget_bytes), float(window_share), ctypes.byref(f),
+                                ctypes.byref(w)))
+    return f.value, w.value
 
 
 def workgroup_xcds(out, num_workgroups, stream=None):

@@ -343,6 +343,50 @@ pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t lay
                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, void* stream);
 
+/* ---- Page pools (host bookkeeping) -------------------------------------------
+ * The two attention groups want different page lifetimes: the sliding group
+ * releases pages the full group still reads (pegainfer issue #807,
+ * Description, first paragraph), so each group gets its own pool and its own
+ * page table (pass it as the pakv_pages of that group's calls).  A window pool
+ * (window W > 0) hands a sequence's pages back once no query that can still
+ * come sees them; the kernels read only pages holding visible positions (an
+ * extend tile may touch one page below the window: its rows are masked, so a
+ * released page, reused or poisoned, changes nothing).
+ *
+ * pakv_page_pool_create: num_pages physical pages for max_seqs sequences of up
+ *   to max_pages_per_seq pages; window 0 for a full pool.
+ * pakv_page_pool_reserve: sequence seq will next store up to position end - 1
+ *   and run queries at first_query or later: it then holds every page with a
+ *   position in [keep_from, end), keep_from = max(0, first_query - W + 1) (0 for
+ *   a full pool), and its pages wholly below keep_from go back to the pool.  A
+ *   decode step with kv_len L has first_query = L - 1, end = L; an extend chunk
+ *   at P has first_query = P, end = P + n.  PAKV_ERR_WORKSPACE, changing
+ *   nothing, when the pool has too few free pages.
+ * pakv_page_pool_release_seq: all of a sequence's pages go back.
+ * pakv_page_pool_table: host int32 [max_seqs][max_pages_per_seq], -1 where no
+ *   page is held; valid until the pool is destroyed.
+ * pakv_page_pool_released: the pages the last reserve / release_seq gave back
+ *   (copies up to cap of them into out; returns how many there were).
+ * Released pages are handed out again last-released first. */
+typedef struct pakv_page_pool pakv_page_pool;
+pakv_status pakv_page_pool_create(int32_t num_pages, int32_t max_seqs, int32_t max_pages_per_seq, int32_t window,
+                                  pakv_page_pool** out);
+void pakv_page_pool_destroy(pakv_page_pool* pool);
+pakv_status pakv_page_pool_reserve(pakv_page_pool* pool, int32_t seq, int32_t first_query, int32_t end);
+pakv_status pakv_page_pool_release_seq(pakv_page_pool* pool, int32_t seq);
+const int32_t* pakv_page_pool_table(const pakv_page_pool* pool);
+int32_t pakv_page_pool_free_pages(const pakv_page_pool* pool);
+int32_t pakv_page_pool_released(const pakv_page_pool* pool, int32_t* out, int32_t cap);
+
+/* Tokens a KV byte budget holds when the window pool keeps window_share
+ * tokens for every token of the full pool (FreeToken PR #898, "End to end":
+ * every printed row has a window pool of one fifth of the full pool, 0.2):
+ * full_tokens = floor(budget / (full_bytes + window_share * window_bytes)),
+ * window_tokens = floor(window_share * full_tokens), with the bytes per token
+ * of pakv_kv_bytes_per_token (owning layers only). */
+pakv_status pakv_pool_tokens(const pakv_layer_map* map, int64_t budget_bytes, double window_share,
+                             int64_t* full_tokens, int64_t* window_tokens);
+
 /* Placement check.  Launches num_workgroups (1 .. 65535) workgroups on
  * stream; workgroup i writes the id of the XCD it ran on to out[i] (device
  * int32 [num_workgroups], caller-owned).  The decode kernel merges a unit's
