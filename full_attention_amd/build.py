@@ -19,7 +19,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-
 # Device code: gfx950 only; packed-FP32 instructions stay off.
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["pakv_api.cpp", "pakv_pool.cpp", "kernels_store.hip", "kernels_decode.hip", "kernels_extend.hip",
+SOURCES = ["pakv_api.cpp", "pakv_pool.cpp", "pakv_step.cpp", "kernels_store.hip", "kernels_decode.hip", "kernels_extend.hip",
            "kernels_extend_general.hip"]
 
 

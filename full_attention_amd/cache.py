@@ -192,3 +192,18 @@ class PagedKVCache:
         pakv.paged_attn_extend_packed(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, k_ext, v_ext, out, nseq,
                                       q.shape[0], max_q_len, max_kv_len, stream)
         return out
+
+    def capture_decode_step(self, kv_lens, max_kv_len, layers_io, buckets, max_batch=None):
+        """A decode step of the given layers captured into one HIP graph per
+        batch-size bucket (pakv_decode_step).  layers_io: (layer, q, out, k_new,
+        v_new) per step layer, tensors sized for max_batch (k_new / v_new None
+        where the rows are stored beforehand); kv_lens: device int32
+        [max_batch], read at every replay.  Run it with step.run(batch)."""
+        if max_batch is None:
+            max_batch = kv_lens.shape[0]
+        need = pakv.DecodeStep.workspace_bytes(self.map, layers_io, max_batch, max_kv_len)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.device)
+        full = self._group_pages["full"][1] if "full" in self._group_pages else self.pages
+        sliding = self._group_pages["sliding"][1] if "sliding" in self._group_pages else None
+        return pakv.DecodeStep(self.map, full, kv_lens, max_batch, max_kv_len, layers_io, buckets, ws,
+                               pages_sliding=sliding)

@@ -189,9 +189,22 @@ __global__ __launch_bounds__(256) void store_q8_kernel(StoreArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void step_positions_kernel(const int32_t* kv_lens, int32_t B, int32_t* cu,
+                                                               int32_t* start) {
+    const int32_t b = blockIdx.x * 256 + threadIdx.x;
+    if (b <= B) cu[b] = b;
+    if (b < B) start[b] = kv_lens[b] - 1;
+}
+
 }  // namespace
 
 namespace pakv {
+
+int launch_step_positions(const int32_t* kv_lens, int32_t B, int32_t* cu, int32_t* start, void* stream) {
+    hipLaunchKernelGGL(step_positions_kernel, dim3((B + 256) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       kv_lens, B, cu, start);
+    return (int)hipGetLastError();
+}
 
 int launch_store(const StoreLaunch& s, void* stream) {
     StoreArgs a;

@@ -41,6 +41,19 @@ int timing_slot(int kind) {
 
 void* const* timing_events() { return g_timing.events; }
 
+TimingPause::TimingPause()
+    : events(g_timing.events), pairs(g_timing.pairs), used(g_timing.used), mask(g_timing.mask) {
+    g_timing.events = nullptr;
+    g_timing.pairs = 0;
+}
+
+TimingPause::~TimingPause() {
+    g_timing.events = events;
+    g_timing.pairs = pairs;
+    g_timing.used = used;
+    g_timing.mask = mask;
+}
+
 DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs) {
     DecodePlan p{};
     p.grid = kDecodeGrid;

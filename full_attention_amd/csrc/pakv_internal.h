@@ -169,5 +169,17 @@ const char* hip_error_string(int err);
 // selected by `kind` (a PAKV_TIME_* bit), or -1; and the caller's event array.
 int timing_slot(int kind);
 void* const* timing_events();
+// Switches the hook off on this thread for the object's lifetime (graph
+// capture: event records inside a graph do not bracket its kernels).
+struct TimingPause {
+    TimingPause();
+    ~TimingPause();
+    void* const* events;
+    int32_t pairs, used, mask;
+};
+
+// cu[b] = b (b <= B) and start[b] = kv_lens[b] - 1 (b < B): the store
+// arguments of one new row per sequence, for a decode step.
+int launch_step_positions(const int32_t* kv_lens, int32_t B, int32_t* cu, int32_t* start, void* stream);
 
 }  // namespace pakv

@@ -36,6 +36,8 @@ EXPORTED = (
     "pakv_paged_attn_decode_noalloc", "pakv_decode_noalloc_max_bytes", "pakv_paged_attn_extend_packed",
     "pakv_page_pool_create", "pakv_page_pool_destroy", "pakv_page_pool_reserve", "pakv_page_pool_release_seq",
     "pakv_page_pool_table", "pakv_page_pool_free_pages", "pakv_page_pool_released", "pakv_pool_tokens",
+    "pakv_decode_step_workspace_bytes", "pakv_decode_step_create", "pakv_decode_step_run",
+    "pakv_decode_step_bucket", "pakv_decode_step_destroy",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -54,6 +56,11 @@ class Slab(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+class StepLayer(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p)]
 
 
 class Pages(ctypes.Structure):
@@ -122,6 +129,17 @@ lib.pakv_page_pool_released.argtypes = [_P, _P, _I]
 lib.pakv_pool_tokens.restype = _I
 lib.pakv_pool_tokens.argtypes = [_P, ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)]
+lib.pakv_decode_step_workspace_bytes.restype = _S
+lib.pakv_decode_step_workspace_bytes.argtypes = [_P, _P, _I, _I, _I]
+lib.pakv_decode_step_create.restype = _I
+lib.pakv_decode_step_create.argtypes = [_P, ctypes.POINTER(Pages), ctypes.POINTER(Pages), _P, _I, _I, _P, _I, _P, _I,
+                                        _P, _S, ctypes.POINTER(_P)]
+lib.pakv_decode_step_run.restype = _I
+lib.pakv_decode_step_run.argtypes = [_P, _I, _P]
+lib.pakv_decode_step_bucket.restype = _I
+lib.pakv_decode_step_bucket.argtypes = [_P, _I]
+lib.pakv_decode_step_destroy.restype = None
+lib.pakv_decode_step_destroy.argtypes = [_P]
 lib.pakv_set_timing_events.restype = _I
 lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
 lib.pakv_timing_pairs_used.restype = _I
@@ -335,6 +353,51 @@ def pool_tokens(layer_map, budget_bytes, window_share):
     _check(lib.pakv_pool_tokens(layer_map.handle, int(budget_bytes), float(window_share), ctypes.byref(f),
                                 ctypes.byref(w)))
     return f.value, w.value
+
+
+class DecodeStep:
+    """Owner of a pakv_decode_step*: the decode step of a layer stack captured
+    into one HIP graph per batch-size bucket.  layers: list of (layer, q, out,
+    k_new, v_new) with tensors sized for max_batch (k_new / v_new None where
+    the rows are stored beforehand); every buffer is kept referenced here, as
+    the graphs hold their addresses."""
+
+    def __init__(self, layer_map, pages_full, kv_lens, max_batch, max_kv_len, layers, buckets, workspace,
+                 pages_sliding=None):
+        arr = (StepLayer * len(layers))(*[StepLayer(l, _ptr(q), _ptr(o), _ptr(kn), _ptr(vn))
+                                          for l, q, o, kn, vn in layers])
+        bk = (_I * len(buckets))(*buckets)
+        handle = _P()
+        _check(lib.pakv_decode_step_create(layer_map.handle, ctypes.byref(pages_full),
+                                           ctypes.byref(pages_sliding) if pages_sliding is not None else None,
+                                           _ptr(kv_lens), max_batch, max_kv_len, ctypes.cast(arr, _P), len(layers),
+                                           ctypes.cast(bk, _P), len(buckets), _ptr(workspace), workspace.numel(),
+                                           ctypes.byref(handle)))
+        self.handle = handle
+        self._keep = (layer_map, pages_full, pages_sliding, kv_lens, layers, workspace)
+
+    @staticmethod
+    def workspace_bytes(layer_map, layers, max_batch, max_kv_len):
+        arr = (StepLayer * len(layers))(*[StepLayer(l, 1, 1, None, None) for l, *_ in layers])
+        return lib.pakv_decode_step_workspace_bytes(layer_map.handle, ctypes.cast(arr, _P), len(layers), max_batch,
+                                                    max_kv_len)
+
+    def run(self, batch, stream=None):
+        _check(lib.pakv_decode_step_run(self.handle, batch, _stream(stream)))
+
+    def bucket(self, batch):
+        return lib.pakv_decode_step_bucket(self.handle, batch)
+
+    def close(self):
+        if self.handle:
+            lib.pakv_decode_step_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def workgroup_xcds(out, num_workgroups, stream=None):

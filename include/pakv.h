@@ -343,6 +343,54 @@ pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t lay
                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, void* stream);
 
+/* ---- Decode step graphs ---------------------------------------------------------
+ * A whole decode step of a layer stack, captured once per batch-size bucket
+ * into a HIP graph and replayed (unsloth commit dee9371: one CUDA graph per
+ * batch-size bucket; commit 749fb75: a single bucket ladder and a single pool
+ * across buckets).  The step runs, on kv_lens (device int32 [max_batch], read at
+ * every replay): one pakv_decode_plan per kind of layer (window, Hkv), then for
+ * each step layer in order: an owning bf16 layer with k_new stores its new row
+ * and decodes in one launch (pakv_paged_attn_decode_append); an owning 8-bit or
+ * K=V layer with k_new runs pakv_paged_kv_store of that row at kv_lens[b] - 1,
+ * then the planned decode; every other layer runs the planned decode.
+ *   layers[i].q, .out          : device bf16 [max_batch][Hq][D]
+ *   layers[i].k_new, .v_new    : device bf16 [max_batch][Hkv][D] (owners), or NULL
+ *                                (the rows were stored before the step)
+ *   pages_full, pages_sliding  : the groups' page tables (pages_sliding NULL:
+ *                                pages_full for every layer)
+ *   workspace                  : device memory of pakv_decode_step_workspace_bytes,
+ *                                zero-filled before the first replay, shared by
+ *                                every bucket; it holds the plans and one decode
+ *                                workspace
+ * Buffers are captured by address: they must stay allocated, and in place,
+ * while the step exists.  pakv_decode_step_run(step, batch, stream) launches
+ * the graph of the smallest bucket >= batch on stream (PAKV_ERR_INVALID above
+ * the largest); rows batch .. bucket - 1 are decoded as well, on what the
+ * caller keeps there: keep their kv_lens at 1 and their page-table rows at -1
+ * (nothing is then written, and they read page 0).  Replays that may overlap
+ * need separate steps and workspaces.  Creating a step captures on a stream of
+ * its own and launches nothing; a call the step makes that its host-side
+ * checks refuse ends the capture, and its status is returned. */
+typedef struct {
+    int32_t layer;
+    const void* q;
+    void* out;
+    const void* k_new;
+    const void* v_new;
+} pakv_step_layer;
+typedef struct pakv_decode_step pakv_decode_step;
+size_t pakv_decode_step_workspace_bytes(const pakv_layer_map* map, const pakv_step_layer* layers, int32_t n_layers,
+                                        int32_t max_batch, int32_t max_kv_len);
+pakv_status pakv_decode_step_create(const pakv_layer_map* map, const pakv_pages* pages_full,
+                                    const pakv_pages* pages_sliding, const int32_t* kv_lens, int32_t max_batch,
+                                    int32_t max_kv_len, const pakv_step_layer* layers, int32_t n_layers,
+                                    const int32_t* buckets, int32_t n_buckets, void* workspace,
+                                    size_t workspace_bytes, pakv_decode_step** out);
+pakv_status pakv_decode_step_run(pakv_decode_step* step, int32_t batch, void* stream);
+/* the bucket a batch runs in, or -1 */
+int32_t pakv_decode_step_bucket(const pakv_decode_step* step, int32_t batch);
+void pakv_decode_step_destroy(pakv_decode_step* step);
+
 /* ---- Page pools (host bookkeeping) -------------------------------------------
  * The two attention groups want different page lifetimes: the sliding group
  * releases pages the full group still reads (pegainfer issue #807,
