@@ -95,6 +95,7 @@ struct DecodeArgs {
     // zeroes the arrival counters of the call's units first
     int32_t zero_arrivals;
     float v_norm_eps;       // K=V layers: eps under the root of the value norm
+    int32_t check_xcd;      // flag and check the XCDs of units merged inside one XCD
 };
 
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
@@ -556,23 +557,30 @@ __device__ __forceinline__ void await(T (&regs)[N]) {
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(regs[i]));
 }
 
-// Counts this workgroup's arrival at a unit and reports whether it was the
-// last of `expected` (then every partial of the unit is complete).  The
-// counter's low 16 bits count arrivals.  On the XCD-local path each workgroup
-// first sets bit 16 + (its XCD) in the same word, and the last to arrive
-// checks that one bit is set in all: a unit whose workgroups ran on several
-// XCDs exchanged its partials through L2s that do not see each other, so the
-// merge may have read stale data, and the status word records it.  (The two
-// atomics of one thread go to one address in order: the first is complete,
-// vmcnt(0), before the second issues.)
-template <bool LOCAL>
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* ticket, uint32_t xcc,
-                                            uint32_t* status) {
-    if (LOCAL && threadIdx.x == 0) {
+// Marks, when a workgroup starts a unit it shares with others inside one XCD,
+// bit 16 + (its XCD) of the unit's counter word.  Issued at the unit's start,
+// without waiting: the wait before the arrival (arrive_last) covers it long
+// after it has landed, so it adds no round trip.
+__device__ __forceinline__ void flag_xcd(uint32_t* counter, uint32_t xcc) {
+    if (threadIdx.x == 0) {
         asm volatile("" : "+s"(xcc));   // form the flag here, not early in the kernel
         __hip_atomic_fetch_or(counter, 1u << (16 + xcc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    wait_vm<0>();               // this wave's partial stores (and the flag) are complete
+}
+
+// Counts this workgroup's arrival at a unit and reports whether it was the
+// last of `expected` (then every partial of the unit is complete).  The
+// counter's low 16 bits count arrivals.  On the XCD-local path every
+// workgroup of the unit set bit 16 + (its XCD) in the same word when it
+// started the unit (flag_xcd), and the last to arrive checks that one bit is
+// set in all: a unit whose workgroups ran on several XCDs exchanged its
+// partials through L2s that do not see each other, so the merge may have read
+// stale data, and the status word records it.  (A workgroup's flag is
+// complete, vmcnt(0), before its arrival issues.)
+template <bool LOCAL>
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* ticket, uint32_t xcc,
+                                            uint32_t* status, bool check) {
+    wait_vm<0>();               // this wave's partial stores (and its flag) are complete
     lds_barrier();              // ... and every wave's
     if (threadIdx.x == 0) {
         uint32_t old;
@@ -581,7 +589,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
         else
             old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *ticket = old;
-        if (LOCAL && (old & 0xffffu) == expected - 1 && (old >> 16) != (1u << xcc))
+        if (LOCAL && check && (old & 0xffffu) == expected - 1 && (old >> 16) != (1u << xcc))
             __hip_atomic_fetch_or(status, kStatusXcdSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     lds_barrier();
@@ -806,6 +814,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
     Unit uc = unit_of(a, st, u_first);
     int32_t kc = min(kc_first, uc.n - 1);
+    // the workgroups [w0, w1] of a unit: from the stream-K run length, or the
+    // aligned split's record (one unit per workgroup there)
+    auto unit_span = [&](const Unit& x, int32_t& w0, int32_t& w1) {
+        w0 = per > 0 ? x.first / per : rw0;
+        w1 = per > 0 ? (x.first + x.n - 1) / per : rw1;
+    };
+    auto flag_if_local = [&](const Unit& x) {
+        int32_t w0, w1;
+        unit_span(x, w0, w1);
+        if (a.check_xcd && xblk > 0 && w0 != w1 && w0 / xblk == w1 / xblk) flag_xcd(a.arrivals + x.u, xcc);
+    };
+    flag_if_local(uc);
     Unit ui = uc;                                 // issue cursor
     int32_t ki = kc;
     const int dq = wave * (D / 4);
@@ -1042,8 +1062,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         // ---- end of this run's part of the unit --------------------------------
         if (kc == uc.n - 1 || i == total - 1) {
             const float l_tot = wave_sum_across_groups(l_run);
-            const int32_t w0 = per > 0 ? uc.first / per : rw0;
-            const int32_t w1 = per > 0 ? (uc.first + uc.n - 1) / per : rw1;
+            int32_t w0, w1;
+            unit_span(uc, w0, w1);
             if (w0 == w1) {
                 // the whole unit is in this run: normalise and write the outputs
                 if (col < G) {
@@ -1068,7 +1088,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                         if (wave == 0 && qg == 0) put2<true>(a.part_ml + (slot + col) * 2, m_run, l_tot);
                     }
                     // the last of the unit's partials to arrive merges them all
-                    if (arrive_last<true>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status)) {
+                    if (arrive_last<true>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status,
+                                          a.check_xcd != 0)) {
                         merge_unit<D, true>(a, uc, w0, w1, G, threadIdx.x);
                         if (threadIdx.x == 0)
                             __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1080,7 +1101,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                         for (int m = 0; m < C::MT; ++m) put4<false>(po + 16 * m + 4 * qg, o[m]);
                         if (wave == 0 && qg == 0) put2<false>(a.part_ml + (slot + col) * 2, m_run, l_tot);
                     }
-                    if (arrive_last<false>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status)) {
+                    if (arrive_last<false>(a.arrivals + uc.u, (uint32_t)(w1 - w0 + 1), &ticket, xcc, a.status,
+                                          false)) {
                         merge_unit<D, false>(a, uc, w0, w1, G, threadIdx.x);
                         if (threadIdx.x == 0)
                             __hip_atomic_store(a.arrivals + uc.u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1094,6 +1116,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         const bool ended = (kc == uc.n - 1);
         advance(a, st, U, uc, kc);
         if (ended && i + 1 < total) {
+            flag_if_local(uc);
             load_q<D>(a, uc, G, col, qg, dq, qreg);
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1178,6 +1201,7 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.append = s.append;
     a.zero_arrivals = s.zero_arrivals;
     a.v_norm_eps = s.v_norm_eps;
+    a.check_xcd = s.check_xcd;
     return a;
 }
 

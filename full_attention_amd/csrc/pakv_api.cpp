@@ -3,6 +3,7 @@
 // the kernel launchers.  Nothing here touches the GPU before every argument has
 // been checked.
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,9 @@ struct TimingHook {
     int32_t mask = 0;
 };
 static thread_local TimingHook g_timing;
+static std::atomic<int32_t> g_decode_checks{0};
+
+int32_t decode_checks() { return g_decode_checks.load(std::memory_order_relaxed); }
 
 pakv_status fail(pakv_status code, const char* fmt, ...) {
     char buf[512];
@@ -117,6 +121,13 @@ pakv_status pakv_set_timing_events(void* const* events, int32_t n_pairs, int32_t
 }
 
 int32_t pakv_timing_pairs_used(void) { return g_timing.used; }
+
+pakv_status pakv_set_decode_checks(int32_t flags) {
+    clear_error();
+    if (flags & ~(int32_t)PAKV_CHECK_XCD_PLACEMENT) return fail(PAKV_ERR_INVALID, "unknown check flags 0x%x", flags);
+    g_decode_checks.store(flags, std::memory_order_relaxed);
+    return PAKV_OK;
+}
 
 pakv_status pakv_resolve_kv_sources(int32_t n_layers, const int32_t* layer_type,
                                     int32_t first_shared, int32_t* out_source) {
@@ -349,6 +360,7 @@ static pakv_status decode_setup(const pakv_layer_map* map, int32_t layer, const 
     a.k_eq_v = S.desc.k_eq_v;
     a.v_norm_eps = S.desc.v_norm_eps;
     a.sm_scale = L.desc.sm_scale;
+    a.check_xcd = (decode_checks() & PAKV_CHECK_XCD_PLACEMENT) ? 1 : 0;
     a.plan = plan_decode(L.desc, num_seqs);
     a.layout = plan_layout(num_seqs, a.hkv, max_kv_len);
     return PAKV_OK;

@@ -124,6 +124,7 @@ struct DecodeLaunch {
     const uint16_t* v_new = nullptr;
     int32_t append = 0;
     int32_t zero_arrivals = 0;   // the plan kernel zeroes the call's counters first
+    int32_t check_xcd = 0;       // pakv_set_decode_checks(PAKV_CHECK_XCD_PLACEMENT)
 };
 int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
 int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched
@@ -164,6 +165,9 @@ int launch_extend(const ExtendLaunch& a, void* stream);           // bf16 K and 
 int launch_extend_general(const ExtendLaunch& a, void* stream);   // 8-bit, K=V, packed chunks
 
 const char* hip_error_string(int err);
+
+// pakv_set_decode_checks flags, read when a decode call is set up
+int32_t decode_checks();
 
 // Timing hook (pakv_set_timing_events): the next event-pair index for a kernel
 // selected by `kind` (a PAKV_TIME_* bit), or -1; and the caller's event array.

@@ -37,11 +37,12 @@ EXPORTED = (
     "pakv_page_pool_create", "pakv_page_pool_destroy", "pakv_page_pool_reserve", "pakv_page_pool_release_seq",
     "pakv_page_pool_table", "pakv_page_pool_free_pages", "pakv_page_pool_released", "pakv_pool_tokens",
     "pakv_decode_step_workspace_bytes", "pakv_decode_step_create", "pakv_decode_step_run",
-    "pakv_decode_step_bucket", "pakv_decode_step_destroy",
+    "pakv_decode_step_bucket", "pakv_decode_step_destroy", "pakv_set_decode_checks",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
 DECODE_PLAN_MISMATCH, DECODE_XCD_SPLIT = 1, 2     # bits of the decode workspace's status word
+CHECK_XCD_PLACEMENT = 1
 
 
 class LayerDesc(ctypes.Structure):
@@ -140,6 +141,8 @@ lib.pakv_decode_step_bucket.restype = _I
 lib.pakv_decode_step_bucket.argtypes = [_P, _I]
 lib.pakv_decode_step_destroy.restype = None
 lib.pakv_decode_step_destroy.argtypes = [_P]
+lib.pakv_set_decode_checks.restype = _I
+lib.pakv_set_decode_checks.argtypes = [_I]
 lib.pakv_set_timing_events.restype = _I
 lib.pakv_set_timing_events.argtypes = [_P, _I, _I]
 lib.pakv_timing_pairs_used.restype = _I
@@ -403,6 +406,10 @@ class DecodeStep:
 def workgroup_xcds(out, num_workgroups, stream=None):
     """out: device int32 [num_workgroups]; out[i] = the XCD workgroup i ran on."""
     return _check(lib.pakv_workgroup_xcds(_ptr(out), num_workgroups, _stream(stream)))
+
+
+def set_decode_checks(flags):
+    return _check(lib.pakv_set_decode_checks(flags))
 
 
 def set_timing_events(events, kernel_mask):

@@ -226,7 +226,8 @@ size_t pakv_decode_workspace_bytes(const pakv_layer_map* map, int32_t layer,
  *                 call then wrote no output and changed nothing else.
  *   PAKV_DECODE_XCD_SPLIT     : some unit merged inside one XCD's L2 had
  *                 workgroups on several XCDs (see pakv_workgroup_xcds); its
- *                 outputs may be wrong.
+ *                 outputs may be wrong.  Checked only while
+ *                 pakv_set_decode_checks(PAKV_CHECK_XCD_PLACEMENT) is on.
  * num_seqs must not exceed 1023 and num_seqs * Hkv 8192 (PAKV_ERR_UNSUPPORTED).
  * A shared layer reads its source's slab (and scales) with its own descriptor
  * (window, sm_scale, Hq).  The keys of all sequences form one stream of
@@ -444,6 +445,18 @@ pakv_status pakv_pool_tokens(const pakv_layer_map* map, int64_t budget_bytes, do
  * call lets a test or a deployment check that on its device.
  * PAKV_ERR_INVALID for a null out or a count out of range. */
 pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream);
+
+/* Optional decode checks, for every decode call made while they are on (a
+ * process-wide setting; 0 turns them off, the default).
+ *   PAKV_CHECK_XCD_PLACEMENT: each workgroup of a unit that merges inside one
+ *     XCD's L2 marks its XCD in the unit's arrival word when it starts the
+ *     unit, and the merging workgroup raises PAKV_DECODE_XCD_SPLIT in the
+ *     status word when more than one XCD took part.  It costs a device-scope
+ *     atomic per such workgroup and unit (about 5% of the E2B-like decode
+ *     step), so it is for tests and bring-up on a new device.
+ * PAKV_ERR_INVALID for unknown bits. */
+#define PAKV_CHECK_XCD_PLACEMENT 1
+pakv_status pakv_set_decode_checks(int32_t flags);
 
 /* Kernel timing hook, for benchmarks and profilers.  events points to 2 *
  * n_pairs hipEvent_t handles (caller-owned, created in the HIP runtime the

@@ -329,3 +329,9 @@ def test_fp8_layers_need_scales_and_share_only_with_fp8():
     with pytest.raises(pakv.PakvError) as e:
         pakv.LayerMap([_desc(dtype=pakv.KV_FP8_PTH), _desc(src=0, dtype=pakv.KV_INT8_PTH)])
     assert e.value.status == pakv.ERR_ALIAS
+
+
+def test_decode_checks_flags():
+    assert pakv.lib.pakv_set_decode_checks(1 << 5) == pakv.ERR_INVALID
+    pakv.set_decode_checks(pakv.CHECK_XCD_PLACEMENT)
+    pakv.set_decode_checks(0)

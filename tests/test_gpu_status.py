@@ -29,7 +29,17 @@ def _workspace_zero_past_status(cache):
 
 
 def test_status_clear_after_local_and_cross_xcd_merges():
+    """With the placement check on (pakv_set_decode_checks)."""
     need_gpu()
+    from full_attention_amd import pakv
+    pakv.set_decode_checks(pakv.CHECK_XCD_PLACEMENT)
+    try:
+        _run_local_and_cross_merges()
+    finally:
+        pakv.set_decode_checks(0)
+
+
+def _run_local_and_cross_merges():
     from full_attention_amd import pakv
     lens = list(np.array(e2b_decode_workload().cached_lens[:60]) + 1) + [5, 17, 100, 250]
     specs = [LayerSpec("full", 512, 8, 1, 0), LayerSpec("sliding", 256, 8, 1, 512)]
