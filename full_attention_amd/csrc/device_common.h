@@ -94,4 +94,18 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word, int byte_lo) 
     return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950).  Each lane gives the LDS
+// byte address of 4 consecutive 16-bit elements, a row of a 16 x 4 block per
+// 16-lane group; lane (a = i % 16 / 4, k = i % 4) of the group receives
+// element k of the rows a, a + 4, a + 8, a + 12 (measured on the device).  So
+// if lane j of group g addresses row 4 g + j / 4, elements 4 (j % 4) .. + 3
+// of a token-major tile, lane i receives one element column (the i-th of the
+// four groups' 16) for the four tokens 4 g .. 4 g + 3: the operand a value
+// product wants from keys stored token-major.
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    auto* lp = (__attribute__((address_space(3))) bf16x4_tr*)(uintptr_t)p;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
 }  // namespace pakv_dev

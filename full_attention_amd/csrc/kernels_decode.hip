@@ -1030,22 +1030,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             if constexpr (F == kFmtBF16) {
                 va = *reinterpret_cast<const u32x2*>(vbuf + d * 32 + ((((qg >> 1) ^ (d >> 3)) & 1) << 4) + 8 * (qg & 1));
             } else if constexpr (F == kFmtKEQV) {
-                // the value operand (one dim, four tokens) from the key rows:
-                // token 4 qg + e's 2-byte element d, in granule (d / 8) ^ token.
-                // (The lane index is made opaque per tile, so that these
-                // addresses are formed where they are read instead of being
-                // held in registers across the chunk loop.)
-                int lid = lane;
-                asm volatile("" : "+v"(lid));
-                const int dd = dq + 16 * m + (lid & 15), rq = 4 * (lid >> 4);
-                uint32_t h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = rq + e;
-                    h[e] = *reinterpret_cast<const uint16_t*>(kbuf + r * C::ROW + ((((dd >> 3) ^ r) & (C::ROW / 16 - 1)) << 4) +
-                                                              (dd & 7) * 2);
-                }
-                va = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                // the value operand (one dim, four tokens) from the key rows,
+                // with one transposing read: lane j of 16-lane group qg
+                // addresses key row 4 qg + j / 4, dims dq + 16 m + 4 (j % 4)
+                // .. + 3 (in granule dim / 8 ^ row), and receives tokens
+                // 4 qg .. + 3 of dim dq + 16 m + col
+                const int r = 4 * qg + (col >> 2);
+                const int dd = dq + 16 * m + 4 * (col & 3);
+                va = lds_read_tr16(kbuf + r * C::ROW + ((((dd >> 3) ^ r) & (C::ROW / 16 - 1)) << 4) + (dd & 7) * 2);
             } else {
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(vbuf + d * 16 + 4 * qg);
                 va = u32x2{codes_to_bf16x2<F>(w, 0), codes_to_bf16x2<F>(w, 2)};
