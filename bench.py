@@ -271,23 +271,50 @@ def time_step(torch, st, steps, warmup, eager):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def host_ahead(torch, step):
+    """A spin kernel to enqueue before an eager step so that the GPU reaches
+    the step only after the host has queued all of it: then each launch starts
+    as the previous one ends, as in a graph replay.  (The start event of
+    hipExtLaunchKernelGGL completes when the GPU reaches it; on an idle GPU
+    that is before the host has submitted the kernel itself, and the host's
+    submission time would be counted as kernel time.)  Returns a callable."""
+    step()                                   # warm: first-call costs stay out of the estimate
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cycles = 1 << 20
+    start.record()
+    torch.cuda._sleep(cycles)
+    stop.record()
+    torch.cuda.synchronize()
+    per_ms = cycles / max(start.elapsed_time(stop), 1e-3)
+    n = int(per_ms * (2.0 * host_ms + 0.5))
+    return lambda: torch.cuda._sleep(n)
+
+
 def kernel_durations(torch, pakv, step, n_launch_per_step, mask, steps):
     """Mean duration (ms) of each selected launch in a step, over `steps`
     eager steps.  The library launches each selected kernel through
     hipExtLaunchKernelGGL with a caller event pair, so the dispatch itself
-    records start and stop: host-side gaps between launches are not counted."""
+    records start and stop; each step is queued behind a spin kernel
+    (host_ahead) so that host-side launch time is not counted either."""
+    ahead = host_ahead(torch, step)
     timing = Timing(torch, pakv, n_launch_per_step * steps)
     torch.cuda.synchronize()
     timing.arm(mask)
     try:
         for _ in range(steps):
+            ahead()
             step()
     finally:
         used = timing.disarm()
     torch.cuda.synchronize()
     assert used == n_launch_per_step * steps, (used, n_launch_per_step, steps)
     d = np.array(timing.durations_ms(used)).reshape(steps, n_launch_per_step)
-    return d.mean(axis=0), "hipExtLaunchKernelGGL events, eager steps"
+    return d.mean(axis=0), "hipExtLaunchKernelGGL events, eager steps queued ahead of the GPU"
 
 
 def cold_calls(torch, pakv, calls, mask, reps):
