@@ -359,7 +359,46 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
         for (int i = t; i <= B; i += 256) S[a.s_soff + i] = st.soff[i];
         for (int i = t; i < B; i += 256) S[a.s_slen + i] = st.slen[i];
     }
-    int32_t* rec = S + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
+    // The record goes to the decode workgroup that runs this run.  The
+    // dispatcher puts decode workgroup i on XCD i mod 8, so XCD x runs the
+    // workgroups x, x + 8, ...; each XCD is given a block of consecutive runs.
+    // Stream-K: blocks of grid / 8 runs.  Aligned split: the R runs are shared
+    // out evenly, block x = [R x / 8, R (x + 1) / 8): with blocks of grid / 8
+    // a sliding layer's 448 runs left one XCD idle (E2B-like step 0.759 ->
+    // 0.755 ms; boundaries moved to unit boundaries, which keeps every merge
+    // inside one XCD but unbalances the blocks, measured slower).
+    // The idle workgroups of each XCD take the runs past R (empty records).
+    // An aligned record also says whether its unit's runs lie in one block
+    // (then the unit's partials stay in that XCD's L2).
+    const int32_t xblk = (a.grid & 7) == 0 ? a.grid >> 3 : 0;
+    int32_t dst = w, local = 0;
+    if (xblk > 0 && !aligned) {
+        dst = (w % xblk) * 8 + w / xblk;
+    } else if (xblk > 0) {
+        const int32_t R = ws_lds[B];                  // <= grid, so R * 8 cannot overflow
+        auto block_start = [&](int32_t x) { return (R * x) >> 3; };
+        auto block_of = [&](int32_t r) {
+            int32_t x = 7;
+            while (x > 0 && block_start(x) > r) --x;
+            return x;
+        };
+        if (w < R) {
+            const int32_t x = block_of(w);
+            dst = (w - block_start(x)) * 8 + x;
+            local = block_of(rw0) == block_of(rw1) ? 1 : 0;
+        } else {
+            int32_t k = w - R;
+            for (int32_t x = 0; x < 8; ++x) {
+                const int32_t n = block_start(x + 1) - block_start(x);
+                if (k < xblk - n) {
+                    dst = (n + k) * 8 + x;
+                    break;
+                }
+                k -= xblk - n;
+            }
+        }
+    }
+    int32_t* rec = S + a.s_rec + (int64_t)dst * pakv::kPlanRecord;
     if (t == 0) {
         rec[0] = c_begin;
         rec[1] = c_end;
@@ -368,6 +407,8 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
         rec[4] = aligned ? 0 : per;
         rec[5] = rw0;
         rec[6] = rw1;
+        rec[7] = w;
+        rec[8] = local;
     }
     for (int32_t j = t; j < max(c_end - c_begin, 64); j += 256) {
         const bool in_run = c_begin + j < c_end;
@@ -763,12 +804,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // the page ids of its first 64 chunks, all loads issued before any wait
     // (one round trip); then Q of the first unit and the first chunks' copies
     // (a second round trip, awaited with the first chunk)
-    // the plan's workgroup index: workgroups go to the XCDs in turn
-    // (blockIdx mod 8), so this numbering gives each XCD a contiguous block
-    // of the plan's runs, and a unit's runs mostly share one XCD's L2
+    // the plan wrote this workgroup's record at its own index: workgroups go
+    // to the XCDs in turn (blockIdx mod 8), and the plan gave each XCD a
+    // contiguous block of its runs, so a unit's runs mostly share one XCD's L2
     const int32_t xblk = (a.grid & 7) == 0 ? a.grid >> 3 : 0;
-    const int32_t vb = xblk > 0 ? (int32_t)(blockIdx.x & 7) * xblk + (int32_t)(blockIdx.x >> 3) : (int32_t)blockIdx.x;
-    const int32_t* rec = a.sched + a.s_rec + (int64_t)vb * pakv::kPlanRecord;
+    const int32_t* rec = a.sched + a.s_rec + (int64_t)blockIdx.x * pakv::kPlanRecord;
     int32_t tab_o[4], tab_l[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {        // B <= 1023: at most four entries per thread
@@ -776,7 +816,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         tab_o[k] = (i <= B) ? a.sched[a.s_soff + i] : 0;
         tab_l[k] = (i < B) ? a.sched[a.s_slen + i] : 1;
     }
-    const int32_t field = rec[min(lane, 7)];
+    const int32_t field = rec[min(lane, 15)];
     const int32_t hdr = a.sched[min(lane, 7)];     // the plan's header
     uint32_t ids = (uint32_t)rec[pakv::kPlanRecIds + lane];
 #pragma unroll
@@ -792,8 +832,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // stream-K runs (per > 0) or unit-aligned runs (per = 0; the unit's
     // workgroups are [rw0, rw1], clamped so that a stale plan stays in bounds)
     const int32_t per = max(__builtin_amdgcn_readlane(field, 4), 0);
+    // the run's number in the plan (it names the run's partial slots)
+    const int32_t vb = clamp_i32(__builtin_amdgcn_readlane(field, 7), 0, a.grid - 1);
     const int32_t rw0 = clamp_i32(__builtin_amdgcn_readlane(field, 5), 0, vb);
     const int32_t rw1 = clamp_i32(__builtin_amdgcn_readlane(field, 6), vb, a.grid - 1);
+    const bool rec_local = __builtin_amdgcn_readlane(field, 8) != 0;
     __syncthreads();
     // a plan made for another shape (sequences, Hkv, window, length bound or
     // grid) describes another split: every workgroup returns before touching
@@ -820,10 +863,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         w0 = per > 0 ? x.first / per : rw0;
         w1 = per > 0 ? (x.first + x.n - 1) / per : rw1;
     };
+    // a unit whose runs all lie in one XCD's block merges in that XCD's L2:
+    // stream-K blocks are grid / 8 runs; the aligned split's record says so
+    auto is_local = [&](int32_t w0, int32_t w1) {
+        return per > 0 ? (xblk > 0 && w0 / xblk == w1 / xblk) : rec_local;
+    };
     auto flag_if_local = [&](const Unit& x) {
         int32_t w0, w1;
         unit_span(x, w0, w1);
-        if (a.check_xcd && xblk > 0 && w0 != w1 && w0 / xblk == w1 / xblk) flag_xcd(a.arrivals + x.u, xcc);
+        if (a.check_xcd && w0 != w1 && is_local(w0, w1)) flag_xcd(a.arrivals + x.u, xcc);
     };
     flag_if_local(uc);
     Unit ui = uc;                                 // issue cursor
@@ -1070,7 +1118,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
                 const int64_t slot = ((int64_t)vb + uc.u) * G;
                 // every run of the unit on one XCD (the check needs no
                 // communication: the split and the numbering are fixed)
-                const bool local = xblk > 0 && w0 / xblk == w1 / xblk;
+                const bool local = is_local(w0, w1);
                 mfma_settle();
                 if (local) {
                     if (col < G) {

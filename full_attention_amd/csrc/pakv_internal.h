@@ -45,15 +45,17 @@ DecodePlan plan_decode(const pakv_layer_desc& d, int32_t num_seqs);
 //                      the unit-aligned split), grid, B, Hkv, window, max_kv_len
 //   soff [B + 1]       first stream chunk of each sequence's units; soff[B] = T
 //   slen [B]           length of each sequence, clamped to [1, max_kv_len]
-//   rec  [grid][kPlanRecord]  per workgroup w of the plan's numbering (the
-//                      decode kernel's workgroup i takes
-//                      w = (i mod 8) * grid / 8 + i / 8, one block of w per
-//                      XCD, when grid is a multiple of 8): first chunk, end chunk, unit of
-//                      the first chunk, that chunk's index in its unit, chunks
-//                      per workgroup (0 for the unit-aligned split), the first
-//                      and last workgroup of its unit (aligned split only),
-//                      spare words, then from word kPlanRecIds the page ids of
-//                      its first 64 chunks (-1 past its run)
+//   rec  [grid][kPlanRecord]  per decode workgroup i, the record of the run
+//                      w it takes (when grid is a multiple of 8, XCD i mod 8
+//                      takes a block of consecutive runs: grid / 8 of them for
+//                      stream-K, an even share of the busy runs for the
+//                      aligned split): first chunk, end chunk, unit of the
+//                      first chunk, that chunk's index in its unit, chunks per
+//                      run (0 for the unit-aligned split), the first and last
+//                      run of its unit (aligned split only), w, whether the
+//                      unit's runs lie in one XCD's block (aligned split
+//                      only), spare words, then from word kPlanRecIds the page
+//                      ids of its first 64 chunks (-1 past its run)
 //   ids  [cap]         page id of every stream chunk (ids outside the pool
 //                      replaced by -1: read as page 0, never written)
 constexpr int32_t kPlanMagic = 0x31504b50;

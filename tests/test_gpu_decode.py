@@ -270,14 +270,21 @@ def test_planned_decode_in_graph_replays():
             assert torch.equal(o, e), f"replay {rep} differs"
 
 
-def _read_plan(plan, B, max_kv_len, hkv=1):
-    """Header and per-workgroup records of a decode plan (the schedule layout the
-    plan and decode kernels share; grid 512)."""
+def _read_plan(plan, B, max_kv_len, hkv=1, by_workgroup=False):
+    """Header and records of a decode plan (the schedule layout the plan and
+    decode kernels share; grid 512).  The plan stores each run's record at the
+    decode workgroup that takes it, with the run's number in word 7; the
+    records come back in run order (words 0..8), or in workgroup order."""
     w = plan.cpu().numpy().view(np.int32)
     soff, slen = 16, 16 + B + 1
     rec = (slen + B + 15) & ~15
     head = w[:8]
-    recs = w[rec:rec + 512 * 80].reshape(512, 80)[:, :7]
+    by_wg = w[rec:rec + 512 * 80].reshape(512, 80)[:, :9]
+    if by_workgroup:
+        return head, by_wg, w[soff:soff + B + 1], w[slen:slen + B]
+    assert sorted(by_wg[:, 7].tolist()) == list(range(512))    # one record per run
+    recs = np.empty_like(by_wg)
+    recs[by_wg[:, 7]] = by_wg
     return head, recs, w[soff:soff + B + 1], w[slen:slen + B]
 
 
@@ -326,17 +333,63 @@ def test_plan_runs_partition_the_stream(case):
     if aligned:
         unit_first = soff[:B]                         # one KV head: unit b starts at soff[b]
         for wg in np.nonzero(busy)[0]:
-            c0, c1, u, kc, per, w0, w1 = (int(x) for x in recs[wg])
+            c0, c1, u, kc, per, w0, w1 = (int(x) for x in recs[wg, :7])
             assert per == 0 and w0 <= wg <= w1
             assert c0 - unit_first[u] == kc and c1 <= unit_first[u] + n[u]       # inside its unit
             assert all(recs[x, 2] == u for x in range(w0, w1 + 1))               # the unit's workgroups
             assert recs[w0, 0] == unit_first[u] and recs[w1, 1] == unit_first[u] + n[u]
 
 
+@pytest.mark.parametrize("case", ["sliding", "full", "skewed"])
+def test_plan_gives_each_xcd_a_block_of_runs(case):
+    """Workgroup i runs on XCD i mod 8.  Aligned split (sliding, full): the R
+    busy runs are shared out evenly, the workgroups of class x taking runs
+    [R x / 8, R (x + 1) / 8) in order and empty records after them, and a
+    record's local flag says whether its unit's runs lie in one such block.
+    Stream-K (skewed): workgroup i takes run (i mod 8) * 64 + i / 8."""
+    need_gpu()
+    from workloads import e2b_decode_workload, make_page_pool
+    from full_attention_amd.cache import PagedKVCache
+    rng = np.random.default_rng(6)
+    if case == "skewed":
+        lens, window = [100000] + [20] * 700, 0
+    else:
+        lens = list(np.array(e2b_decode_workload().cached_lens) + 1)
+        window = 512 if case == "sliding" else 0
+    spec = LayerSpec("sliding" if window else "full", 256, 8, 1, window)
+    pool = make_page_pool(rng, lens)
+    cache = PagedKVCache([spec], None, pool.num_pages, sentinel=False)
+    cache.set_page_table(pool.page_table)
+    B, maxl = len(lens), max(lens)
+    plan = cache.decode_plan(0, i32(lens), maxl)
+    torch.cuda.synchronize()
+    head, wg, _, _ = _read_plan(plan, B, maxl, by_workgroup=True)
+    runs = wg[:, 7]
+    if head[2] != 0:
+        assert case == "skewed"
+        i = np.arange(512)
+        assert np.array_equal(runs, (i % 8) * 64 + i // 8)
+        return
+    busy = wg[:, 0] < wg[:, 1]
+    R = int(busy.sum())
+    start = [(R * x) // 8 for x in range(9)]
+    if case == "sliding":
+        assert R == 448 and all(start[x + 1] - start[x] == 56 for x in range(8))   # every XCD busy
+    block = lambda r: max(x for x in range(8) if start[x] <= r)
+    for x in range(8):
+        cls = runs[x::8]
+        n = start[x + 1] - start[x]
+        assert np.array_equal(cls[:n], np.arange(start[x], start[x + 1]))
+        assert np.all(~busy[x::8][n:]) and np.all(cls[n:] >= R)
+    for i in np.nonzero(busy)[0]:
+        w0, w1 = int(wg[i, 5]), int(wg[i, 6])
+        assert wg[i, 8] == (1 if block(w0) == block(w1) else 0)
+
+
 def test_merges_inside_and_across_xcd_blocks():
-    """Workgroup i runs the plan's workgroup (i mod 8) * 64 + i / 8, so each XCD
-    holds a block of 64 consecutive plan workgroups; a unit whose workgroups lie
-    in one block merges through that XCD's L2, the others through memory.  The
+    """The plan gives each XCD (the workgroups of one class mod 8) a block of
+    consecutive runs, the busy runs shared out evenly; a unit whose runs lie in
+    one block merges through that XCD's L2, the others through memory.  The
     E2B full-layer length mix has units of both kinds (checked on the plan);
     four short sequences added to it give single-workgroup units.  Every output
     matches the oracle."""
@@ -355,9 +408,9 @@ def test_merges_inside_and_across_xcd_blocks():
     head, recs, _, _ = _read_plan(plan, B, maxl)
     assert head[2] == 0                                   # the unit-aligned split
     busy = recs[:, 0] < recs[:, 1]
-    spans = {(int(recs[w, 5]), int(recs[w, 6])) for w in np.nonzero(busy)[0]}
-    inside = [s for s in spans if s[0] < s[1] and s[0] // 64 == s[1] // 64]
-    across = [s for s in spans if s[0] // 64 != s[1] // 64]
+    spans = {(int(recs[w, 5]), int(recs[w, 6]), int(recs[w, 8])) for w in np.nonzero(busy)[0]}
+    inside = [s for s in spans if s[0] < s[1] and s[2] == 1]
+    across = [s for s in spans if s[0] < s[1] and s[2] == 0]
     single = [s for s in spans if s[0] == s[1]]
     assert inside and across and single, (len(inside), len(across), len(single))
     ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
