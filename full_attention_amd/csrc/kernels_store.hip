@@ -100,6 +100,112 @@ __global__ __launch_bounds__(256) void store_bf16_kernel(StoreArgs a) {
     for (int e = 0; e < EPL; ++e) vdst[(lane * EPL + e) * kPage] = vv[e];
 }
 
+// Chunk stores (many tokens per sequence): one workgroup per 16 consecutive
+// tokens of the flat list and KV head.  The row kernel writes a token's V row
+// as D scattered 2-byte stores into the dim-major page; here the 16 rows are
+// staged in LDS and, when they fill one page (slots 0 .. 15 of one page, as
+// every block does where sequences start and end on page boundaries), each
+// dim's 16 values go out as one contiguous 32-byte row.  Other blocks write
+// each present token's values one by one, as the row kernel does.
+//
+// Where the 16 tokens go: a block inside one sequence (the usual case) needs
+// the sequence (a 64-way search by wave 0), its start position and at most
+// two page-table entries; a block that crosses sequences searches each token
+// (lanes 0 .. 15, binary search over cu_tokens).  Rows whose position falls
+// outside the page table or the pool are dropped, as in the row kernel.
+template <int D>
+__global__ __launch_bounds__(256) void store_bf16_pages_kernel(StoreArgs a) {
+    constexpr int CPR = D / 8;                 // 16-byte pieces per row
+    constexpr int PER_T = 16 * CPR / 256;      // pieces per thread (2 or 4)
+    __shared__ int64_t head_of[16];            // phys page * hkv + h, or -1
+    __shared__ int32_t slot_of[16];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[16 * D];
+    const int t = threadIdx.x, lane = t & 63;
+    const int32_t t0 = blockIdx.x * 16;
+    const int32_t h = blockIdx.y;
+    const int32_t nt = min(16, a.total_tokens - t0);
+    const bool has_v = a.v != nullptr;
+    // the rows themselves do not depend on where they go: fetch them first
+    u32x4 kr[PER_T], vr[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int idx = t + 256 * i, j = idx / CPR, c = idx % CPR;
+        const int64_t src = ((int64_t)(t0 + j) * a.hkv + h) * D + c * 8;
+        if (j < nt) {
+            kr[i] = *reinterpret_cast<const u32x4*>(a.k + src);
+            if (has_v) vr[i] = *reinterpret_cast<const u32x4*>(a.v + src);
+        }
+    }
+    if (t < 64) {
+        const int32_t b = find_seq(a.cu_tokens, a.num_seqs, t0, lane);
+        const int32_t cb = a.cu_tokens[b], ce = a.cu_tokens[b + 1];
+        const bool one_seq = t0 + nt <= ce;     // every token of the block is in sequence b
+        int32_t bj = b, rel = t0 + lane - cb;
+        if (!one_seq && lane < nt) {
+            int32_t lo = 0, hi = a.num_seqs - 1;  // the last sequence with cu <= token
+            const int32_t tok = t0 + lane;
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (a.cu_tokens[mid] <= tok) lo = mid; else hi = mid - 1;
+            }
+            bj = lo;
+            rel = tok - a.cu_tokens[lo];
+        }
+        if (lane < 16) {
+            int64_t ph = -1;
+            int32_t slot = 0;
+            if (lane < nt) {
+                const int32_t pos = a.start_pos[bj] + rel;
+                const int32_t pg = pos >> 4;
+                if (pos >= 0 && pg < a.max_pages) {
+                    const int32_t phys = a.page_table[(int64_t)bj * a.max_pages + pg];
+                    if ((uint32_t)phys < (uint32_t)a.num_pages) {
+                        ph = (int64_t)phys * a.hkv + h;
+                        slot = pos & 15;
+                    }
+                }
+            }
+            head_of[lane] = ph;
+            slot_of[lane] = slot;
+        }
+    }
+    if (has_v) {
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int idx = t + 256 * i, j = idx / CPR;
+            if (j < nt) *reinterpret_cast<u32x4*>(vs + idx * 8) = vr[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int idx = t + 256 * i, j = idx / CPR, c = idx % CPR;
+        if (j < nt && head_of[j] >= 0)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.k_slab) + (head_of[j] * kPage + slot_of[j]) * D +
+                                      c * 8) = kr[i];
+    }
+    if (!has_v) return;
+    bool whole = nt == 16 && head_of[0] >= 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) whole = whole && head_of[j] == head_of[0] && slot_of[j] == j;
+#pragma unroll
+    for (int dd = 0; dd < D / 256; ++dd) {
+        const int d = t + 256 * dd;
+        uint16_t* vrow = reinterpret_cast<uint16_t*>(a.v_slab) + d * kPage;
+        if (whole) {
+            uint32_t w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (uint32_t)vs[(2 * e) * D + d] | ((uint32_t)vs[(2 * e + 1) * D + d] << 16);
+            u32x4* dst = reinterpret_cast<u32x4*>(vrow + head_of[0] * kPage * D);
+            dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+            dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+        } else {
+            for (int j = 0; j < nt; ++j)
+                if (head_of[j] >= 0) vrow[head_of[j] * kPage * D + slot_of[j]] = vs[j * D + d];
+        }
+    }
+}
+
 // Nearest OCP E4M3 code of y (ties to even mantissa), saturating at +-448:
 // below 2^-6 the grid is the multiples of 2^-9 (y * 512 is exact, and a
 // result of 8 is the first normal code); above, y = f * 2^e with f in [1, 2)
@@ -225,7 +331,12 @@ int launch_store(const StoreLaunch& s, void* stream) {
     dim3 grid((s.total_tokens + 3) / 4, s.hkv);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int K = PAKV_TIME_STORE;
-    if (s.kv_dtype == PAKV_KV_BF16) {
+    if (s.kv_dtype == PAKV_KV_BF16 && s.total_tokens >= 4 * s.num_seqs) {
+        // chunks (on average four or more tokens per sequence): whole V pages
+        const dim3 pgrid((s.total_tokens + 15) / 16, s.hkv);
+        if (s.head_dim == 256) launch(K, store_bf16_pages_kernel<256>, pgrid, dim3(256), 0, st, a);
+        else launch(K, store_bf16_pages_kernel<512>, pgrid, dim3(256), 0, st, a);
+    } else if (s.kv_dtype == PAKV_KV_BF16) {
         if (s.head_dim == 256) launch(K, store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
         else launch(K, store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
     } else if (s.kv_dtype == PAKV_KV_FP8_PTH) {

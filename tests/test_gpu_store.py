@@ -43,6 +43,108 @@ def test_store_bf16_bit_exact(d, hkv):
     assert (vh.transpose(0, 3, 1, 2)[~written] == 0x7FC0).all()
 
 
+def _check_bf16_slab(sc, k, v, starts, counts, table, hkv, dropped=()):
+    """Every stored row bit for bit where its page walk leads (rows of `dropped`
+    (b, i) pairs nowhere), and the NaN sentinel in every other slot."""
+    ks = host_bits(sc.cache.slabs[0][0])
+    vs = host_bits(sc.cache.slabs[0][1]) if v is not None else None
+    cu = np.concatenate([[0], np.cumsum(counts)])
+    written = np.zeros((sc.pool.num_pages, 16), dtype=bool)
+    for b in range(len(counts)):
+        for i in range(counts[b]):
+            if (b, i) in dropped:
+                continue
+            pos = starts[b] + i
+            written[table[b, pos // 16], pos % 16] = True
+            for h in range(hkv):
+                assert np.array_equal(page_walk_k(ks, table, b, pos, h), k[cu[b] + i, h])
+                if vs is not None:
+                    assert np.array_equal(page_walk_v(vs, table, b, pos, h), v[cu[b] + i, h])
+    assert (ks.transpose(0, 2, 1, 3)[~written] == 0x7FC0).all()
+    if vs is not None:
+        assert (vs.transpose(0, 3, 1, 2)[~written] == 0x7FC0).all()
+
+
+@pytest.mark.parametrize("case", ["whole_pages", "ragged", "one_token_each", "k_eq_v"])
+@pytest.mark.parametrize("d,hkv", [(256, 1), (512, 2)])
+def test_store_bf16_paths_bit_exact(case, d, hkv):
+    """Chunks of four or more tokens per sequence on average go through the
+    kernel that writes whole V pages (32-byte dim rows when 16 tokens fill a
+    page, single values otherwise); fewer go through the row kernel.  Both
+    are bit-exact: whole pages only (page-aligned starts and counts), ragged
+    starts and ends with blocks of 16 tokens that cross sequences, one token
+    per sequence, and a K=V layer (keys only)."""
+    need_gpu()
+    if case == "whole_pages":
+        caps, starts, counts = [64, 32, 96, 16], [0, 16, 32, 0], [64, 16, 48, 16]
+    elif case == "one_token_each":
+        caps = [1, 17, 33, 16, 5, 200, 31, 2]
+        starts, counts = [c - 1 for c in caps], [1] * 8
+    else:
+        caps, starts, counts = [40, 7, 100, 33, 19], [3, 0, 21, 32, 2], [37, 7, 79, 1, 17]
+    spec = LayerSpec("full", d, hkv, hkv, 0, k_eq_v=(case == "k_eq_v"))
+    sc = Scenario([spec], None, caps, seed=61 + d + len(case))
+    k, v = sc.store(0, starts, counts)
+    torch.cuda.synchronize()
+    _check_bf16_slab(sc, k, None if case == "k_eq_v" else v, starts, counts, sc.pool.page_table, hkv)
+
+
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("chunk", [True, False])
+def test_store_drops_rows_without_a_page(d, chunk):
+    """A position whose page-table entry lies outside the pool, or whose page
+    index lies past the table's width, is dropped; every other row lands, in
+    both store kernels."""
+    need_gpu()
+    caps = [48, 40, 64]
+    spec = LayerSpec("full", d, 1, 1, 0)
+    sc = Scenario([spec], None, caps, seed=73 + d)
+    table = sc.pool.page_table.copy()
+    table[0, 1] = sc.pool.num_pages + 3          # page 1 of sequence 0: outside the pool
+    table[2, 2] = -1                             # page 2 of sequence 2: no page
+    sc.cache.set_page_table(table)
+    width = table.shape[1]
+    if chunk:
+        starts, counts = [0, 8, 16], [48, 32, 48]
+    else:
+        starts, counts = [20, 39, 40], [1, 1, 1]
+    # one more sequence: the last slot of the table's last page, then a row
+    # past the table's width
+    starts2 = starts + [width * 16 - (1 if chunk else 0)]
+    counts2 = counts + [2 if chunk else 1]
+    B = len(starts2)
+    table4 = np.concatenate([table, np.full((1, width), -1, np.int32)], axis=0)
+    table4[3, width - 1] = sc.pool.spare_pages[0]   # the last page in the table: a spare one
+    sc.cache.set_page_table(table4)
+    total = sum(counts2)
+    k = normal_bf16(sc.rng, (total, 1, d))
+    v = normal_bf16(sc.rng, (total, 1, d))
+    cu = np.concatenate([[0], np.cumsum(counts2)]).astype(np.int32)
+    sc.cache.store(0, i32(cu), i32(starts2), dev_bits(k), dev_bits(v))
+    torch.cuda.synchronize()
+    dropped = set()
+    for b in range(B):
+        for i in range(counts2[b]):
+            pos = starts2[b] + i
+            if pos // 16 >= width or not (0 <= table4[b, pos // 16] < sc.pool.num_pages):
+                dropped.add((b, i))
+    assert dropped                                  # the case drops something
+    assert len(dropped) < total                     # and stores the rest
+    ks, vs = host_bits(sc.cache.slabs[0][0]), host_bits(sc.cache.slabs[0][1])
+    written = np.zeros((sc.pool.num_pages, 16), dtype=bool)
+    for b in range(B):
+        for i in range(counts2[b]):
+            if (b, i) in dropped:
+                continue
+            pos = starts2[b] + i
+            page = table4[b, pos // 16]
+            written[page, pos % 16] = True
+            assert np.array_equal(ks[page, 0, pos % 16], k[cu[b] + i, 0])
+            assert np.array_equal(vs[page, 0, :, pos % 16], v[cu[b] + i, 0])
+    assert (ks.transpose(0, 2, 1, 3)[~written] == 0x7FC0).all()
+    assert (vs.transpose(0, 3, 1, 2)[~written] == 0x7FC0).all()
+
+
 @pytest.mark.parametrize("d", [256, 512])
 def test_store_int8_matches_oracle_encoding(d):
     need_gpu()
