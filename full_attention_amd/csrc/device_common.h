@@ -108,4 +108,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
+// Page-table entries outside the pool (or positions past a table's width)
+// are read as page 0, or dropped by a store, in every build.  A build with
+// PAKV_DEBUG_BOUNDS also counts them, per kind of call, in the library's
+// counter array (`bad` is its device address; null in other builds).
+constexpr int kBadIdPlan = 0, kBadIdStore = 1, kBadIdExtend = 2;
+__device__ __forceinline__ void note_bad_id(uint32_t* bad, int kind) {
+#ifdef PAKV_DEBUG_BOUNDS
+    if (bad) __hip_atomic_fetch_add(bad + kind, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    (void)bad;
+    (void)kind;
+#endif
+}
+
 }  // namespace pakv_dev

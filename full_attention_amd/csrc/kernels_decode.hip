@@ -96,6 +96,7 @@ struct DecodeArgs {
     int32_t zero_arrivals;
     float v_norm_eps;       // K=V layers: eps under the root of the value norm
     int32_t check_xcd;      // flag and check the XCDs of units merged inside one XCD
+    uint32_t* bad_ids;      // counters of a PAKV_DEBUG_BOUNDS build, else null
 };
 
 // Waits for this wave's copies so that at most `newer` chunks' copies stay in
@@ -237,7 +238,9 @@ __device__ __forceinline__ uint32_t page_of_chunk(const DecodeArgs& a, const int
     const int32_t n = chunks_of(a, len);
     const int32_t k = (c - st.soff[b]) % n;
     const int32_t ph = page_table[(int64_t)b * a.max_pages + (window_lo(a, len) >> 4) + k];
-    return ((uint32_t)ph < (uint32_t)a.num_pages) ? (uint32_t)ph : kNoPage;
+    if ((uint32_t)ph < (uint32_t)a.num_pages) return (uint32_t)ph;
+    note_bad_id(a.bad_ids, kBadIdPlan);
+    return kNoPage;
 }
 
 // Prefix over sequences of the decode workgroups an aligned split gives them
@@ -1242,6 +1245,7 @@ static DecodeArgs args_of(const DecodeLaunch& s) {
     a.zero_arrivals = s.zero_arrivals;
     a.v_norm_eps = s.v_norm_eps;
     a.check_xcd = s.check_xcd;
+    a.bad_ids = debug_bad_ids_ptr();
     return a;
 }
 

@@ -168,6 +168,7 @@ struct ExtendArgs {
     int32_t group;
     int32_t window;
     float score_scale;   // sm_scale * log2(e)
+    uint32_t* bad_ids;   // counters of a PAKV_DEBUG_BOUNDS build, else null
 };
 
 // XOR key of a kv token's K row in LDS (16-byte granules).  LDS serves a
@@ -515,9 +516,12 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
     auto load_ids = [&](int32_t c) -> int32_t {
         const int32_t pg = page0 + 64 * c + lane;
-        int32_t ph = 0;
+        int32_t ph = -1;
         if (pg < a.max_pages) ph = pt[pg];
-        return ((uint32_t)ph < (uint32_t)a.num_pages) ? ph : 0;
+        if ((uint32_t)ph < (uint32_t)a.num_pages) return ph;
+        // counted once per workgroup, for pages holding visible keys
+        if (wave == 0 && 16 * pg < hi && 16 * pg + 16 > lo) note_bad_id(a.bad_ids, kBadIdExtend);
+        return 0;
     };
     // ids holds pages [64 c_ids, +64), ids_next the next 64.  Only the K copy
     // reads page ids (V(t) copies the pages K(t) did, a step later), and a
@@ -797,6 +801,7 @@ int launch_extend(const ExtendLaunch& s, void* stream) {
     a.v_slab = static_cast<const uint16_t*>(s.slab.v);
     a.num_pages = s.slab.num_pages;
     a.page_table = s.page_table;
+    a.bad_ids = debug_bad_ids_ptr();
     a.max_pages = s.max_pages;
     a.cu_q = s.cu_q;
     a.prefix_lens = s.prefix_lens;

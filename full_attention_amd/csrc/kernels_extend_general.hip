@@ -71,6 +71,7 @@ struct GenArgs {
     int32_t window;
     float score_scale;          // sm_scale * log2(e)
     float v_norm_eps;
+    uint32_t* bad_ids;          // counters of a PAKV_DEBUG_BOUNDS build, else null
 };
 
 template <int D, int F>
@@ -186,9 +187,13 @@ __global__ __launch_bounds__(256, (D == 256 ? 2 : 1)) void extend_general_kernel
     const int tau = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
 
     const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+    // (called only for pages that hold visible keys)
     auto page_of = [&](int32_t pos) -> int64_t {
-        int32_t ph = (pos >> 4) < a.max_pages ? pt[pos >> 4] : 0;
-        ph = ((uint32_t)ph < (uint32_t)a.num_pages) ? ph : 0;
+        int32_t ph = (pos >> 4) < a.max_pages ? pt[pos >> 4] : -1;
+        if ((uint32_t)ph >= (uint32_t)a.num_pages) {
+            note_bad_id(a.bad_ids, kBadIdExtend);
+            ph = 0;
+        }
         return (int64_t)ph * a.hkv + g;      // (page, head) block index
     };
 
@@ -420,6 +425,7 @@ int launch_extend_general(const ExtendLaunch& s, void* stream) {
     a.v_scale = s.slab.v_scale;
     a.num_pages = s.slab.num_pages;
     a.page_table = s.page_table;
+    a.bad_ids = debug_bad_ids_ptr();
     a.max_pages = s.max_pages;
     a.cu_q = s.cu_q;
     a.prefix_lens = s.prefix_lens;

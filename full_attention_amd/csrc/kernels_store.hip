@@ -12,6 +12,8 @@
 // K pages are token-major ([16][D]); V pages are dim-major ([D][16]), so a V
 // row lands as D strided 2-byte (or 1-byte) stores.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch_timing.h"
 #include "pakv_internal.h"
@@ -35,6 +37,7 @@ struct StoreArgs {
     int32_t num_seqs;
     int32_t total_tokens;
     int32_t hkv;
+    uint32_t* bad_ids;      // counters of a PAKV_DEBUG_BOUNDS build, else null
 };
 
 // Sequence of token t: the last b with cu_tokens[b] <= t, found by the 64 lanes
@@ -60,11 +63,12 @@ __device__ __forceinline__ bool locate(const StoreArgs& a, int32_t t, int32_t h,
                                        int64_t& page_head, int32_t& slot) {
     const int32_t b = find_seq(a.cu_tokens, a.num_seqs, t, lane);
     const int32_t pos = a.start_pos[b] + (t - a.cu_tokens[b]);
-    if (pos < 0) return false;
     const int32_t pg = pos >> 4;
-    if (pg >= a.max_pages) return false;
-    const int32_t phys = a.page_table[(int64_t)b * a.max_pages + pg];
-    if ((uint32_t)phys >= (uint32_t)a.num_pages) return false;
+    const int32_t phys = (pos >= 0 && pg < a.max_pages) ? a.page_table[(int64_t)b * a.max_pages + pg] : -1;
+    if ((uint32_t)phys >= (uint32_t)a.num_pages) {
+        if (lane == 0) note_bad_id(a.bad_ids, kBadIdStore);
+        return false;
+    }
     page_head = (int64_t)phys * a.hkv + h;
     slot = pos & 15;
     return true;
@@ -157,12 +161,13 @@ __global__ __launch_bounds__(256) void store_bf16_pages_kernel(StoreArgs a) {
             if (lane < nt) {
                 const int32_t pos = a.start_pos[bj] + rel;
                 const int32_t pg = pos >> 4;
-                if (pos >= 0 && pg < a.max_pages) {
-                    const int32_t phys = a.page_table[(int64_t)bj * a.max_pages + pg];
-                    if ((uint32_t)phys < (uint32_t)a.num_pages) {
-                        ph = (int64_t)phys * a.hkv + h;
-                        slot = pos & 15;
-                    }
+                const int32_t phys =
+                    (pos >= 0 && pg < a.max_pages) ? a.page_table[(int64_t)bj * a.max_pages + pg] : -1;
+                if ((uint32_t)phys < (uint32_t)a.num_pages) {
+                    ph = (int64_t)phys * a.hkv + h;
+                    slot = pos & 15;
+                } else {
+                    note_bad_id(a.bad_ids, kBadIdStore);
                 }
             }
             head_of[lane] = ph;
@@ -302,9 +307,46 @@ __global__ __launch_bounds__(256) void step_positions_kernel(const int32_t* kv_l
     if (b < B) start[b] = kv_lens[b] - 1;
 }
 
+// The counters of a PAKV_DEBUG_BOUNDS build (kBadId* kinds), one copy per
+// GPU; host code uses the address debug_bad_ids_ptr() takes, never the name.
+__device__ __align__(256) uint32_t debug_bad_ids[pakv::kDebugCounters];
+
 }  // namespace
 
 namespace pakv {
+
+uint32_t* debug_bad_ids_ptr() {
+#ifdef PAKV_DEBUG_BOUNDS
+    static std::mutex mu;
+    static uint32_t* per_device[kNoallocMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_bad_ids)) != hipSuccess) return nullptr;
+        per_device[dev] = static_cast<uint32_t*>(p);
+    }
+    return per_device[dev];
+#else
+    return nullptr;
+#endif
+}
+
+int debug_bad_ids_read(uint32_t* out, int n) {
+    uint32_t* p = debug_bad_ids_ptr();
+    if (!p || n < 0 || n > kDebugCounters) return (int)hipErrorInvalidValue;
+    if (hipError_t e = hipDeviceSynchronize()) return (int)e;
+    return (int)hipMemcpy(out, p, sizeof(uint32_t) * n, hipMemcpyDeviceToHost);
+}
+
+int debug_bad_ids_reset() {
+    uint32_t* p = debug_bad_ids_ptr();
+    if (!p) return (int)hipErrorInvalidValue;
+    const uint32_t zeros[kDebugCounters] = {};
+    if (hipError_t e = hipDeviceSynchronize()) return (int)e;
+    return (int)hipMemcpy(p, zeros, sizeof zeros, hipMemcpyHostToDevice);
+}
 
 int launch_step_positions(const int32_t* kv_lens, int32_t B, int32_t* cu, int32_t* start, void* stream) {
     hipLaunchKernelGGL(step_positions_kernel, dim3((B + 256) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
@@ -328,6 +370,7 @@ int launch_store(const StoreLaunch& s, void* stream) {
     a.num_seqs = s.num_seqs;
     a.total_tokens = s.total_tokens;
     a.hkv = s.hkv;
+    a.bad_ids = debug_bad_ids_ptr();
     dim3 grid((s.total_tokens + 3) / 4, s.hkv);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int K = PAKV_TIME_STORE;

@@ -204,10 +204,35 @@ pakv_status pakv_layer_map_create(const pakv_layer_desc* descs, int32_t n, pakv_
         std::memset(&m->layers[l].slab, 0, sizeof(pakv_slab));
     }
     *out = m;
+    // a PAKV_DEBUG_BOUNDS build takes its counters' device address here,
+    // before any call that a caller may capture into a graph
+    (void)debug_bad_ids_ptr();
     return PAKV_OK;
 }
 
 void pakv_layer_map_destroy(pakv_layer_map* map) { delete map; }
+
+static pakv_status hip_status(int err, const char* what);
+
+pakv_status pakv_debug_bounds_counts(uint32_t* counts) {
+    clear_error();
+#ifdef PAKV_DEBUG_BOUNDS
+    if (!counts) return fail(PAKV_ERR_INVALID, "counts is null");
+    return hip_status(debug_bad_ids_read(counts, PAKV_DEBUG_COUNTS), "debug_bounds_counts");
+#else
+    (void)counts;
+    return fail(PAKV_ERR_UNSUPPORTED, "page ids are counted only by a PAKV_DEBUG_BOUNDS build");
+#endif
+}
+
+pakv_status pakv_debug_bounds_reset(void) {
+    clear_error();
+#ifdef PAKV_DEBUG_BOUNDS
+    return hip_status(debug_bad_ids_reset(), "debug_bounds_reset");
+#else
+    return fail(PAKV_ERR_UNSUPPORTED, "page ids are counted only by a PAKV_DEBUG_BOUNDS build");
+#endif
+}
 
 pakv_status pakv_layer_map_bind_slab(pakv_layer_map* map, int32_t layer, const pakv_slab* slab) {
     clear_error();

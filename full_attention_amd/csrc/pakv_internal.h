@@ -140,6 +140,14 @@ constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
 constexpr int kNoallocMaxDevices = 64;
 int noalloc_scratch(void** ptr);
 
+// The counters of a PAKV_DEBUG_BOUNDS build (uint32_t[kDebugCounters], a
+// file-scope device array): the current device's address, taken once per
+// device; null in other builds, and on error.
+constexpr int kDebugCounters = 4;
+uint32_t* debug_bad_ids_ptr();
+int debug_bad_ids_read(uint32_t* out, int n);   // waits for the device; hipError_t
+int debug_bad_ids_reset();                      // waits for the device; hipError_t
+
 struct ExtendLaunch {
     SlabView slab;
     const int32_t* page_table;

@@ -15,7 +15,9 @@ import os
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpakv.so")
+# PAKV_LIBRARY selects another build of the library (the diagnostic builds
+# beside libpakv.so: libpakv_bounds.so, libpakv_hostsan.so)
+LIB_PATH = os.environ.get("PAKV_LIBRARY") or os.path.join(_HERE, "libpakv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -38,11 +40,13 @@ EXPORTED = (
     "pakv_page_pool_table", "pakv_page_pool_free_pages", "pakv_page_pool_released", "pakv_pool_tokens",
     "pakv_decode_step_workspace_bytes", "pakv_decode_step_create", "pakv_decode_step_run",
     "pakv_decode_step_bucket", "pakv_decode_step_destroy", "pakv_set_decode_checks",
+    "pakv_debug_bounds_counts", "pakv_debug_bounds_reset",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
 DECODE_PLAN_MISMATCH, DECODE_XCD_SPLIT = 1, 2     # bits of the decode workspace's status word
 CHECK_XCD_PLACEMENT = 1
+DEBUG_COUNTS = 3                                  # decode plans, stores, extend calls
 
 
 class LayerDesc(ctypes.Structure):
@@ -149,6 +153,10 @@ lib.pakv_timing_pairs_used.restype = _I
 lib.pakv_timing_pairs_used.argtypes = []
 lib.pakv_workgroup_xcds.restype = _I
 lib.pakv_workgroup_xcds.argtypes = [_P, _I, _P]
+lib.pakv_debug_bounds_counts.restype = _I
+lib.pakv_debug_bounds_counts.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+lib.pakv_debug_bounds_reset.restype = _I
+lib.pakv_debug_bounds_reset.argtypes = []
 
 
 class PakvError(RuntimeError):
@@ -410,6 +418,19 @@ def workgroup_xcds(out, num_workgroups, stream=None):
 
 def set_decode_checks(flags):
     return _check(lib.pakv_set_decode_checks(flags))
+
+
+def debug_bounds_counts():
+    """Page-table entries outside the pool met on the current device since the
+    last reset: (decode plans, stores, extend calls).  PAKV_DEBUG_BOUNDS builds
+    only (PakvError with ERR_UNSUPPORTED otherwise)."""
+    out = (ctypes.c_uint32 * DEBUG_COUNTS)()
+    _check(lib.pakv_debug_bounds_counts(out))
+    return tuple(int(x) for x in out)
+
+
+def debug_bounds_reset():
+    return _check(lib.pakv_debug_bounds_reset())
 
 
 def set_timing_events(events, kernel_mask):

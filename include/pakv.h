@@ -458,6 +458,24 @@ pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stre
 #define PAKV_CHECK_XCD_PLACEMENT 1
 pakv_status pakv_set_decode_checks(int32_t flags);
 
+/* Page-id bounds diagnostics.  In every build, a page-table entry outside
+ * [0, num_pages) met for a position a call uses (or a position past the
+ * table's width) never moves an access outside the slab: decode and extend
+ * read page 0 in its place (wrong values for those keys), and a store drops
+ * the row.  A build with PAKV_DEBUG_BOUNDS defined (libpakv_bounds.so, built
+ * beside libpakv.so) also counts them on the device, per kind:
+ *   counts[0]  entries met by decode plans (pakv_decode_plan and the calls
+ *              that plan for themselves), once per chunk;
+ *   counts[1]  rows dropped by pakv_paged_kv_store;
+ *   counts[2]  entries met by extend calls, once per workgroup that reads
+ *              the page (so a bad page may count several times).
+ * The counts belong to the current device and add up over calls until
+ * pakv_debug_bounds_reset.  Both calls first wait for all work on the current
+ * device.  Other builds: PAKV_ERR_UNSUPPORTED (nothing is counted there). */
+#define PAKV_DEBUG_COUNTS 3
+pakv_status pakv_debug_bounds_counts(uint32_t counts[PAKV_DEBUG_COUNTS]);
+pakv_status pakv_debug_bounds_reset(void);
+
 /* Kernel timing hook, for benchmarks and profilers.  events points to 2 *
  * n_pairs hipEvent_t handles (caller-owned, created in the HIP runtime the
  * library runs in); while the hook is set, each store / decode / extend call

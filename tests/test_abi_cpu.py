@@ -6,6 +6,7 @@ returned before anything is launched."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -335,3 +336,30 @@ def test_decode_checks_flags():
     assert pakv.lib.pakv_set_decode_checks(1 << 5) == pakv.ERR_INVALID
     pakv.set_decode_checks(pakv.CHECK_XCD_PLACEMENT)
     pakv.set_decode_checks(0)
+
+
+def test_debug_bounds_calls_refused_by_the_product_build():
+    """The page-id counters exist only in a PAKV_DEBUG_BOUNDS build; the
+    product library refuses both calls on the host, touching no device."""
+    if os.path.basename(pakv.LIB_PATH) == "libpakv_bounds.so":
+        pytest.skip("this process loaded the PAKV_DEBUG_BOUNDS build")
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.debug_bounds_counts()
+    assert e.value.status == pakv.ERR_UNSUPPORTED
+    with pytest.raises(pakv.PakvError) as e:
+        pakv.debug_bounds_reset()
+    assert e.value.status == pakv.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("variant", ["bounds", "hostsan"])
+def test_diagnostic_builds_export_every_declared_symbol(variant):
+    """libpakv_bounds.so (PAKV_DEBUG_BOUNDS) and libpakv_hostsan.so (host code
+    under ASan/UBSan) are the same ABI: every symbol the header declares."""
+    from full_attention_amd.build import library_path
+    path = library_path(variant)
+    if not os.path.exists(path):
+        pytest.skip(f"{os.path.basename(path)} is not built (__graft_entry__.build() builds it)")
+    nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pakv_[a-z0-9_]+)\b", nm))
+    missing = [n for n in declared_symbols() if n not in exported]
+    assert not missing, missing
