@@ -245,10 +245,15 @@ class LayerMap:
 
 
 def make_pages(page_table, num_seqs=None, max_pages_per_seq=None):
-    """pakv_pages for a device int32 [B, max_pages] tensor."""
+    """pakv_pages for a device int32 [B, max_pages] tensor.  The struct holds
+    the tensor's address, so it also keeps the tensor alive: a temporary table
+    freed while its pages struct is in use would let later allocations reuse
+    the memory the kernels read page ids from."""
     if num_seqs is None:
         num_seqs, max_pages_per_seq = page_table.shape
-    return Pages(_ptr(page_table), num_seqs, max_pages_per_seq)
+    pages = Pages(_ptr(page_table), num_seqs, max_pages_per_seq)
+    pages._table = page_table
+    return pages
 
 
 def paged_kv_store(layer_map, layer, pages, cu_tokens, start_pos, k, v, num_seqs, total_tokens, stream=None):

@@ -363,3 +363,20 @@ def test_diagnostic_builds_export_every_declared_symbol(variant):
     exported = set(re.findall(r"\bT (pakv_[a-z0-9_]+)\b", nm))
     missing = [n for n in declared_symbols() if n not in exported]
     assert not missing, missing
+
+
+def test_pages_struct_keeps_its_table_alive():
+    """make_pages holds a reference to the table tensor, so a temporary table
+    cannot be freed (and its memory reused) while the struct is in use."""
+    import gc
+    import weakref
+    import torch
+    t = torch.zeros((3, 4), dtype=torch.int32)
+    ref = weakref.ref(t)
+    pages = pakv.make_pages(t)
+    del t
+    gc.collect()
+    assert ref() is not None and pages.num_seqs == 3 and pages.max_pages_per_seq == 4
+    del pages
+    gc.collect()
+    assert ref() is None

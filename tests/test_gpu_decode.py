@@ -112,6 +112,44 @@ def test_other_sequences_change_nothing_but_the_partition():
     assert_close(alone[0], ref, "alone")
 
 
+@pytest.mark.parametrize("window", [0, 512])
+def test_same_split_gives_the_same_bits_in_any_batch(window):
+    """A unit's split depends only on its length and on the batch's chunks per
+    run.  Batches with the same lengths (so the same split) give a sequence
+    bit-identical output wherever it sits in the batch and whatever its
+    neighbours hold, although its runs land on other workgroups (and its merge
+    may go through one XCD's L2 in one batch and through memory in another)."""
+    need_gpu()
+    from full_attention_amd import pakv
+    from workloads import normal_bf16
+    d = 512 if window == 0 else 256
+    spec = LayerSpec("full" if window == 0 else "sliding", d, 8, 1, window)
+    lens = [1800, 900, 3100, 2600, 700, 1300]      # sequence 0 is the one followed
+    alt = lens[1:]                                  # neighbours of the same lengths, other data
+    every = lens + alt
+    sc = Scenario([spec], None, every, seed=81)
+    sc.store(0, [0] * len(every), every)
+    q_all = normal_bf16(np.random.default_rng(82), (len(every), 8, d))
+    table = sc.pool.page_table
+
+    def run(rows):
+        L = [every[r] for r in rows]
+        saved = sc.cache.pages
+        sc.cache.pages = pakv.make_pages(torch.as_tensor(table[rows], dtype=torch.int32).cuda())
+        out = host_bits(sc.cache.decode(0, i32(L), dev_bits(q_all[rows]), max(L)))
+        torch.cuda.synchronize()
+        sc.cache.pages = saved
+        return out
+
+    n = len(lens)
+    a = run([0, 1, 2, 3, 4, 5])
+    b = run([3, 5, 1, 0, 2, 4])                     # the same sequences in another order
+    c = run([0] + [n + i for i in range(len(alt))])  # sequence 0 beside other data
+    assert np.array_equal(a[0], b[3]), "another position in the batch changed the bits"
+    assert np.array_equal(a[0], c[0]), "other neighbours changed the bits"
+    assert_close(a[0], sc.oracle.decode(0, 0, q_all[0], lens[0]))
+
+
 def test_shared_layers_read_their_source():
     need_gpu()
     specs = [LayerSpec("sliding", 256, 8, 1, 64), LayerSpec("full", 512, 8, 1, 0),
