@@ -29,6 +29,9 @@
  *    never allocates, frees or copies device memory, never synchronises, and
  *    never reads device memory from the host: every call is asynchronous on the
  *    stream it is given (a hipStream_t passed as void*; NULL is the null stream).
+ *    The one exception is the pair of page-id diagnostic calls of a
+ *    PAKV_DEBUG_BOUNDS build (pakv_debug_bounds_counts / _reset), which wait
+ *    for the device and copy their counters.
  *  - bf16 tensors are 16-bit bfloat16 bit patterns.  Page size is 16 tokens.
  *  - Device-side values (lengths, page ids) are clamped into range so that no
  *    access leaves the buffers the descriptors describe: a length above the
