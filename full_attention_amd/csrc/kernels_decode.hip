@@ -274,11 +274,11 @@ __device__ __forceinline__ void build_wg_table(const DecodeArgs& a, const SeqTab
     __syncthreads();
 }
 
-// The schedule of a decode call (the plan): every workgroup of the plan
-// kernel builds the sequence table, takes run w = blockIdx.x of the chunk
-// stream (the decode workgroup whose plan numbering is w will stream it) and
-// writes its record and the page ids of its chunks; workgroup 0 also writes
-// the header and the table.
+// The schedule of a decode call (the plan): every workgroup of a plan builds
+// the sequence table, takes run w (its index among the plan's grid
+// workgroups) of the chunk stream and writes its record (at the decode
+// workgroup that will stream it) and the page ids of its chunks; the
+// workgroup of run 0 also writes the header and the table.
 //
 // Runs hold at most per chunks.  When giving every unit its own
 // ceil(n / per) workgroups fits the grid for some per no more than an eighth
@@ -289,8 +289,8 @@ __device__ __forceinline__ void build_wg_table(const DecodeArgs& a, const SeqTab
 // are equal contiguous pieces of ceil(T / grid) chunks (stream-K).  Record fields: c_begin, c_end, first unit, its first
 // chunk, then per for stream-K, or 0 and the first and last workgroup of the
 // unit for the aligned split.
-__global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
-                                                           const int32_t* __restrict__ kv_lens) {
+__device__ __forceinline__ void plan_body(const DecodeArgs& a, const int32_t* __restrict__ page_table,
+                                          const int32_t* __restrict__ kv_lens, int32_t w, int32_t n_wg) {
     __shared__ int32_t seq_lds[2 * (pakv::kDecodeMaxSeqs + 1)];
     __shared__ int32_t ws_lds[pakv::kDecodeMaxSeqs + 1];
     const SeqTable st{seq_lds, seq_lds + pakv::kDecodeMaxSeqs + 1};
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
     if (a.zero_arrivals) {
         // the decode kernel runs after this kernel ends (stream order), and
         // counts its arrivals from zero
-        for (int32_t i = blockIdx.x * 256 + t; i < B * a.hkv; i += gridDim.x * 256) a.arrivals[i] = 0u;
+        for (int32_t i = w * 256 + t; i < B * a.hkv; i += n_wg * 256) a.arrivals[i] = 0u;
     }
     build_seq_table(a, kv_lens, st, B);
     const int32_t T = st.soff[B];
@@ -317,7 +317,6 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
             break;
         }
     }
-    const int32_t w = blockIdx.x;
     int32_t c_begin, c_end, u = 0, kc = 0, rw0 = 0, rw1 = 0;
     if (aligned) {
         c_begin = c_end = T;
@@ -352,7 +351,7 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
         }
     }
     int32_t* S = a.sched;
-    if (blockIdx.x == 0) {
+    if (w == 0) {
         if (t == 0) {
             const int32_t head[8] = {pakv::kPlanMagic, T, aligned ? 0 : per, a.grid, B, a.hkv, a.window,
                                      a.max_kv_len};
@@ -419,6 +418,23 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const in
         if (j < 64) rec[pakv::kPlanRecIds + j] = (int32_t)id;
         if (in_run) S[a.s_ids + c_begin + j] = (int32_t)id;
     }
+}
+
+// One plan (workgroup w takes run w), or the two plans of a decode step's two
+// kinds of layer in one launch (the first grid's workgroups take the first;
+// the plans are independent and each alone is bound by its round trips).
+// Each calls the body with its own kernel parameters.
+__global__ __launch_bounds__(256) void decode_plan_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
+                                                           const int32_t* __restrict__ kv_lens) {
+    plan_body(a, page_table, kv_lens, (int32_t)blockIdx.x, (int32_t)gridDim.x);
+}
+
+__global__ __launch_bounds__(256) void decode_plan2_kernel(DecodeArgs a0, DecodeArgs a1,
+                                                            const int32_t* __restrict__ page_table0,
+                                                            const int32_t* __restrict__ page_table1,
+                                                            const int32_t* __restrict__ kv_lens) {
+    if ((int32_t)blockIdx.x < a0.grid) plan_body(a0, page_table0, kv_lens, (int32_t)blockIdx.x, a0.grid);
+    else plan_body(a1, page_table1, kv_lens, (int32_t)blockIdx.x - a0.grid, a1.grid);
 }
 
 // Page ids of stream chunks c0 .. c0 + count - 1 from the schedule (lane j
@@ -1253,6 +1269,13 @@ int launch_decode_plan(const DecodeLaunch& s, void* stream) {
     const DecodeArgs a = args_of(s);
     hipLaunchKernelGGL(decode_plan_kernel, dim3(s.plan.grid), dim3(256), 0, static_cast<hipStream_t>(stream), a,
                        s.page_table, s.kv_lens);
+    return (int)hipGetLastError();
+}
+
+int launch_decode_plan2(const DecodeLaunch& s0, const DecodeLaunch& s1, void* stream) {
+    const DecodeArgs a0 = args_of(s0), a1 = args_of(s1);
+    hipLaunchKernelGGL(decode_plan2_kernel, dim3(s0.plan.grid + s1.plan.grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a0, a1, s0.page_table, s1.page_table, s0.kv_lens);
     return (int)hipGetLastError();
 }
 

@@ -620,3 +620,25 @@ pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stre
 }
 
 }  // extern "C"
+
+// The plans of two layers (of different kinds) from the same kv_lens, in one
+// launch; the same checks as pakv_decode_plan for each.
+pakv_status pakv::decode_plan_pair(const pakv_layer_map* map, const int32_t layer[2], const pakv_pages* const pages[2],
+                                   const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                                   void* const plan[2], const size_t plan_bytes[2], void* stream) {
+    clear_error();
+    DecodeLaunch a[2];
+    for (int k = 0; k < 2; ++k) {
+        if (pakv_status s = decode_setup(map, layer[k], pages[k], num_seqs, max_kv_len, a[k])) return s;
+        const size_t need = decode_plan_bytes(map->layers[layer[k]].desc, num_seqs, max_kv_len);
+        if (!plan[k] || plan_bytes[k] < need)
+            return fail(PAKV_ERR_WORKSPACE, "decode plan needs %zu bytes, got %zu", need,
+                        plan[k] ? plan_bytes[k] : (size_t)0);
+        a[k].kv_lens = kv_lens;
+        a[k].sched = static_cast<int32_t*>(plan[k]);
+    }
+    if (num_seqs == 0) return PAKV_OK;
+    if (!kv_lens) return fail(PAKV_ERR_INVALID, "kv_lens is null");
+    return hip_status(launch_decode_plan2(a[0], a[1], stream), "decode_plan launch");
+}
+

@@ -129,6 +129,11 @@ struct DecodeLaunch {
     int32_t check_xcd = 0;       // pakv_set_decode_checks(PAKV_CHECK_XCD_PLACEMENT)
 };
 int launch_decode_plan(const DecodeLaunch& a, void* stream);   // writes a.sched from kv_lens, page_table
+// two plans (a decode step's two kinds of layer, same kv_lens) in one launch
+int launch_decode_plan2(const DecodeLaunch& a0, const DecodeLaunch& a1, void* stream);
+pakv_status decode_plan_pair(const pakv_layer_map* map, const int32_t layer[2], const pakv_pages* const pages[2],
+                             const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len, void* const plan[2],
+                             const size_t plan_bytes[2], void* stream);
 int launch_decode(const DecodeLaunch& a, void* stream);        // reads a.sched
 int launch_xcd_probe(int32_t* out, int32_t n, void* stream);  // out[i] = XCD of workgroup i
 

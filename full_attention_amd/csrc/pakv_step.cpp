@@ -110,11 +110,21 @@ static pakv_status enqueue_step(const pakv_layer_map* map, const pakv_pages* pag
     if (need_pos)
         if (int e = launch_step_positions(kv_lens, B, cu, start, s)) return fail(PAKV_ERR_HIP, "step positions: %s",
                                                                                  hip_error_string(e));
-    for (size_t k = 0; k < kinds.rep.size(); ++k) {
-        const int32_t r = kinds.rep[k];
-        if (pakv_status st = pakv_decode_plan(map, r, pages_of(r), kv_lens, B, max_kv_len, ws + lay.plan_off[k],
-                                              lay.plan_bytes[k], s))
-            return st;
+    if (kinds.rep.size() == 2) {
+        // both kinds' plans in one launch: they are independent, and each is
+        // bound by its round trips rather than by its work
+        const int32_t rep[2] = {kinds.rep[0], kinds.rep[1]};
+        const pakv_pages* pg[2] = {pages_of(rep[0]), pages_of(rep[1])};
+        void* const plans[2] = {ws + lay.plan_off[0], ws + lay.plan_off[1]};
+        const size_t bytes[2] = {lay.plan_bytes[0], lay.plan_bytes[1]};
+        if (pakv_status st = decode_plan_pair(map, rep, pg, kv_lens, B, max_kv_len, plans, bytes, s)) return st;
+    } else {
+        for (size_t k = 0; k < kinds.rep.size(); ++k) {
+            const int32_t r = kinds.rep[k];
+            if (pakv_status st = pakv_decode_plan(map, r, pages_of(r), kv_lens, B, max_kv_len, ws + lay.plan_off[k],
+                                                  lay.plan_bytes[k], s))
+                return st;
+        }
     }
     for (int32_t i = 0; i < n; ++i) {
         const int32_t l = layers[i].layer;
