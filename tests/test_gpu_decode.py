@@ -64,6 +64,20 @@ def test_long_context_many_splits():
         assert_close(got, ref, f"long {kv_dtype}")
 
 
+@pytest.mark.parametrize("window,hkv", [(0, 1), (32, 8)])
+def test_largest_batch_per_call(window, hkv):
+    """1023 sequences, the most one decode call takes (the per-sequence table
+    the kernels keep in LDS is then full), of lengths 1..60; at Hkv 8 that is
+    8184 (sequence, KV head) units, near the 8192 a call takes.  Every output
+    matches the oracle."""
+    need_gpu()
+    rng = np.random.default_rng(91 + hkv)
+    lens = [int(x) for x in rng.integers(1, 61, 1023)]
+    sc = _decode_case(256, 8, hkv, window, "bf16", lens, seed=93 + hkv)
+    got, ref, _ = sc.decode(0, lens)
+    assert_close(got, ref, f"1023 sequences, W {window}, Hkv {hkv}")
+
+
 def test_deterministic_and_page_placement_invariant():
     need_gpu()
     lens = [37, 1000, 513, 4096]
