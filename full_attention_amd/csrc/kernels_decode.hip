@@ -281,7 +281,7 @@ __device__ __forceinline__ void build_wg_table(const DecodeArgs& a, const SeqTab
 // workgroup of run 0 also writes the header and the table.
 //
 // Runs hold at most per chunks.  When giving every unit its own
-// ceil(n / per) workgroups fits the grid for some per no more than an eighth
+// ceil(n / per) workgroups fits the grid for some per no more than a half
 // above ceil(T / grid) (units few, or of similar length, like a sliding
 // window's), each unit is split evenly over its own workgroups and no run
 // crosses a unit: a run that crosses one writes two partials and reloads Q in
@@ -303,13 +303,16 @@ __device__ __forceinline__ void plan_body(const DecodeArgs& a, const int32_t* __
     }
     build_seq_table(a, kv_lens, st, B);
     const int32_t T = st.soff[B];
-    // the aligned split may lengthen the longest run by up to an eighth (at
+    // the aligned split may lengthen the longest run by up to a half (at
     // least one chunk): the full layers of the E2B-like step need one more
-    // chunk per run to align, and gain (59.7 -> 58.0 us)
+    // chunk per run to align, and gain (59.7 -> 58.0 us); the 26B-like
+    // sliding layers (units of 65 chunks, 49 per run even) take one run per
+    // unit at 65 and merge nothing, instead of stream-K runs that each cross
+    // a unit (step 2.66 -> 2.56 ms)
     const int32_t per0 = max((T + a.grid - 1) / a.grid, 1);
     int32_t per = per0;
     bool aligned = false;
-    for (int32_t p = per0; p <= per0 + max(per0 / 8, 1); ++p) {
+    for (int32_t p = per0; p <= per0 + max(per0 / 2, 1); ++p) {
         build_wg_table(a, st, B, p, ws_lds);
         if (ws_lds[B] <= a.grid) {
             aligned = true;
