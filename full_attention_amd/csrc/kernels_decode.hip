@@ -312,7 +312,28 @@ __device__ __forceinline__ void plan_body(const DecodeArgs& a, const int32_t* __
     const int32_t per0 = max((T + a.grid - 1) / a.grid, 1);
     int32_t per = per0;
     bool aligned = false;
-    for (int32_t p = per0; p <= per0 + max(per0 / 2, 1); ++p) {
+    // Small batches (under 4 chunks per workgroup on average): filling the
+    // grid cut a unit into as many runs as it has chunks, and its merging
+    // workgroup then read them all, 7 or 8 per round trip.  The runs of a
+    // unit are capped (16 on sliding layers, whose units are short, 32 on
+    // full ones), measured over the batch buckets of the E2B-like step:
+    // batch 1 0.565 -> 0.380 ms, batch 8 0.587 -> 0.417 ms, batch 16
+    // 0.566 -> 0.500 ms per step; 32 and 64 unchanged.
+    int32_t p_min = per0;
+    if (per0 < 4) {
+        __shared__ int32_t nmax_w[kWaves];
+        int32_t m = 0;
+        for (int32_t b = t; b < B; b += 256) m = max(m, chunks_of(a, st.slen[b]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+        if ((t & 63) == 0) nmax_w[t >> 6] = m;
+        __syncthreads();
+        int32_t nmax = nmax_w[0];
+        for (int w2 = 1; w2 < kWaves; ++w2) nmax = max(nmax, nmax_w[w2]);
+        const int32_t cap = a.window > 0 ? 16 : 32;
+        p_min = max(per0, (nmax + cap - 1) / cap);
+    }
+    for (int32_t p = p_min; p <= p_min + max(p_min / 2, 1); ++p) {
         build_wg_table(a, st, B, p, ws_lds);
         if (ws_lds[B] <= a.grid) {
             aligned = true;

@@ -438,6 +438,38 @@ def test_plan_gives_each_xcd_a_block_of_runs(case):
         assert wg[i, 8] == (1 if block(w0) == block(w1) else 0)
 
 
+@pytest.mark.parametrize("window,lens,cap", [(0, [4000], 32), (0, [3000, 700, 5], 32), (512, [2000, 600], 16)])
+def test_small_batches_cap_the_runs_of_a_unit(window, lens, cap):
+    """Under 4 chunks per workgroup on average, no unit is cut into more than
+    16 runs on a sliding layer, 32 on a full one (checked on the plan), and the
+    outputs match the oracle."""
+    need_gpu()
+    from full_attention_amd.cache import PagedKVCache
+    from workloads import make_page_pool, normal_bf16
+    d = 256 if window else 512
+    spec = LayerSpec("sliding" if window else "full", d, 8, 1, window)
+    sc = Scenario([spec], None, lens, seed=97)
+    starts = [max(0, L - window) if window else 0 for L in lens]
+    sc.store(0, starts, [L - s0 for L, s0 in zip(lens, starts)])
+    B, maxl = len(lens), max(lens)
+    kv = i32(lens)
+    plan = sc.cache.decode_plan(0, kv, maxl)
+    q = normal_bf16(np.random.default_rng(98), (B, 8, d))
+    out = host_bits(sc.cache.decode(0, kv, dev_bits(q), maxl, plan=plan))
+    torch.cuda.synchronize()
+    head, recs, soff, _ = _read_plan(plan, B, maxl)
+    assert head[2] == 0                                   # unit-aligned
+    busy = recs[:, 0] < recs[:, 1]
+    units = recs[busy, 2]
+    runs = np.bincount(units, minlength=B)
+    L = np.array(lens)
+    n = (L + 15) // 16 - (np.maximum(0, L - window) // 16 if window else 0)
+    assert -(-int(n.sum()) // 512) < 4                     # the small-batch case
+    assert runs.max() <= cap and (runs[n > cap] > 1).all(), runs
+    ref = np.stack([sc.oracle.decode(0, b, q[b], Lb) for b, Lb in enumerate(lens)])
+    assert_close(out, ref)
+
+
 def test_merges_inside_and_across_xcd_blocks():
     """The plan gives each XCD (the workgroups of one class mod 8) a block of
     consecutive runs, the busy runs shared out evenly; a unit whose runs lie in
