@@ -342,6 +342,23 @@ def cold_calls(torch, pakv, calls, mask, reps):
     return med
 
 
+def batch_ladder(torch, st, reps=30):
+    """The captured step replayed for the first B sequences, for each batch
+    bucket B of the ladder up to the workload's batch: milliseconds per step
+    (latency of smaller batches; the headline is the full batch)."""
+    out = {}
+    for b in [x for x in LADDER if x <= st["B"]]:
+        for _ in range(5):
+            st["step"].run(b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            st["step"].run(b)
+        torch.cuda.synchronize()
+        out[str(b)] = round((time.perf_counter() - t0) * 1e3 / reps, 4)
+    return out
+
+
 def decode_report(torch, pakv, st, args, wl_name, config):
     """The JSON object of one decode workload: warm step, roofline of the
     dominant kernel, cold per-call aggregate."""
@@ -373,6 +390,8 @@ def decode_report(torch, pakv, st, args, wl_name, config):
            "config": dict(config, workload=config["workload"], algorithmic_bytes_per_step=int(step_bytes),
                           launch="eager" if args.eager else "HIP graph replay (pakv_decode_step)"),
            "roofline": roofline}
+    if not args.eager:
+        rep["ms_per_step_by_batch"] = batch_ladder(torch, st)
     if not args.no_cold:
         eager_plans(st)
         med = cold_calls(torch, pakv, [lambda l=l: eager_layer(st, l) for l in range(nl)], pakv.TIME_DECODE,
@@ -589,6 +608,8 @@ def main():
                     "+ 20 shared layers decode"})
         line.update(value=rep["value"], ms_per_step=rep["ms_per_step"], config=rep["config"],
                     frac_of_hbm_peak=rep["frac_of_hbm_peak"], roofline=rep["roofline"])
+        if "ms_per_step_by_batch" in rep:
+            line["ms_per_step_by_batch"] = rep["ms_per_step_by_batch"]
         if "cold" in rep:
             line["cold"] = rep["cold"]
         progress(f"E2B-like decode: {rep['value']} GB/s")
