@@ -501,6 +501,53 @@ def test_merges_inside_and_across_xcd_blocks():
     assert_close(out, ref)
 
 
+@pytest.mark.parametrize("d,hq,hkv,kv_dtype,lens,local", [
+    (512, 16, 1, "bf16", [4000] * 8, 1),        # 63 runs a unit, each unit in one XCD block
+    (256, 16, 2, "int8", [4000] * 8, 1),        # 32 runs a unit, two units a block
+    (512, 8, 1, "bf16", [4000], 0),             # 32 runs over every block
+    (256, 8, 1, "fp8", [9000, 3000, 700], 0),   # 32 + 11 + 3 runs
+])
+def test_units_of_many_runs_merge(d, hq, hkv, kv_dtype, lens, local):
+    """Units cut into many runs (up to 63, so that the merge takes several
+    batches of 7 partials at D 512, 8 at 256, with a ragged last one), merged
+    inside one XCD's L2 or across XCDs as the case says (checked on the plan).
+    The outputs match the oracle and are bit-identical over three calls, the
+    placement check finds nothing, and the arrival counters are zero after
+    each call."""
+    need_gpu()
+    from full_attention_amd import pakv
+    gs = 7 if d == 512 else 8
+    sc = _decode_case(d, hq, hkv, 0, kv_dtype, lens, seed=59)
+    B, maxl = len(lens), max(lens)
+    kv = i32(lens)
+    plan = sc.cache.decode_plan(0, kv, maxl)
+    torch.cuda.synchronize()
+    head, recs, _, _ = _read_plan(plan, B, maxl, hkv=hkv)
+    assert head[2] == 0                                   # unit-aligned
+    busy = recs[:, 0] < recs[:, 1]
+    spans = {(int(recs[w, 5]), int(recs[w, 6]), int(recs[w, 8])) for w in np.nonzero(busy)[0]}
+    many = [sp for sp in spans if sp[1] - sp[0] + 1 > 2 * gs]
+    assert many and all(sp[2] == local for sp in many), sorted(spans)
+    q = normal_bf16(np.random.default_rng(60), (B, hq, d))
+    ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
+    pakv.set_decode_checks(pakv.CHECK_XCD_PLACEMENT)
+    try:
+        first = None
+        for _ in range(3):
+            out = host_bits(sc.cache.decode(0, kv, dev_bits(q), maxl, plan=plan))
+            torch.cuda.synchronize()
+            if first is None:
+                assert_close(out, ref)
+                first = out
+            else:
+                assert np.array_equal(out, first)
+            assert sc.cache.status() == 0
+            w = sc.cache._workspace.cpu().numpy()
+            assert not w[4:256 + 4 * 8192].any()
+    finally:
+        pakv.set_decode_checks(0)
+
+
 def test_workgroups_of_one_class_mod_8_share_an_xcd():
     """The decode merge keeps a unit's partials in one XCD's L2 when all of its
     workgroups lie in one class of i mod 8, which is correct only if those
