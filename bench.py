@@ -72,6 +72,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     ap.add_argument("--only", choices=["e2b", "26b", "int8", "extend"], default=None,
                     help="run one workload only (profiling runs)")
+    ap.add_argument("--no-ladder", action="store_true",
+                    help="skip the per-batch-bucket step times (profiling runs: every dispatch is then one of "
+                         "the full batch)")
     return ap.parse_args()
 
 
@@ -390,7 +393,7 @@ def decode_report(torch, pakv, st, args, wl_name, config):
            "config": dict(config, workload=config["workload"], algorithmic_bytes_per_step=int(step_bytes),
                           launch="eager" if args.eager else "HIP graph replay (pakv_decode_step)"),
            "roofline": roofline}
-    if not args.eager:
+    if not args.eager and not args.no_ladder:
         rep["ms_per_step_by_batch"] = batch_ladder(torch, st)
     if not args.no_cold:
         eager_plans(st)
