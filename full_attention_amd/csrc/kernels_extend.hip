@@ -291,6 +291,15 @@ __device__ __forceinline__ void copy_piece(bool is_k, int i, const uint8_t* src,
 // and add them to the row sum; stage 6 packs the first kv half into pb0.  The
 // second half is packed by softmax_pack_hi once the value MFMAs of the
 // current tile no longer read pb1.
+// The lane id, recomputed where it is used (the asm keeps the compiler from
+// holding it, or a value derived from it, across the main loop: the D = 256
+// kernel has no register to spare for them and spilled them to scratch).
+__device__ __forceinline__ int32_t lane_id_here() {
+    int32_t v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+
 struct SoftRow {
     float mx;
     float m_use;
@@ -298,13 +307,29 @@ struct SoftRow {
     bool raise;
 };
 
+// The row's visible kv range is [row_lo, row_hi].  FRESH (the D = 256
+// kernel): row_lo holds the row's position instead, and the range (lower end
+// position - window + 1 on a sliding layer, upper min(position, hi - 1), given
+// as row_hi) and the lane's 8h are formed here, out of values the compiler
+// cannot hoist: kept across the loop they took registers it does not have.
+template <bool FRESH>
 __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, int32_t t0, bool whole,
-                                              int32_t row_lo, int32_t row_hi, int h, float score_scale,
-                                              float& m_run, float& l_run, u32x4& pb0) {
+                                              int32_t row_lo, int32_t row_hi, int32_t window, int h,
+                                              float score_scale, float& m_run, float& l_run, u32x4& pb0) {
     if (stage == 0) {
         if (!whole) {
             // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
-            const int32_t lo_l = row_lo - t0 - 8 * h, hi_l = row_hi - t0 - 8 * h;
+            int32_t lo_l, hi_l;
+            if constexpr (FRESH) {
+                const int32_t h8 = (lane_id_here() >> 5) << 3;
+                int32_t pos = row_lo;
+                asm volatile("" : "+v"(pos));
+                lo_l = (window > 0 ? pos - window + 1 : -(1 << 30)) - t0 - h8;
+                hi_l = min(pos, row_hi) - t0 - h8;
+            } else {
+                lo_l = row_lo - t0 - 8 * h;
+                hi_l = row_hi - t0 - 8 * h;
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int c = e + ((e >> 3) << 3);
@@ -488,7 +513,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     const int32_t lo = (a.window > 0) ? max(0, prefix + tok_first - a.window + 1) : 0;
 
     // this lane's query rows (one per row block: score column) and their
-    // visible kv ranges [row_lo, row_hi]; a row block past the chunk is idle
+    // visible kv ranges [row_lo, row_hi] (at D = 256 the position and hi - 1:
+    // the softmax forms the range); a row block past the chunk is idle
     const int32_t wrow0 = row0 + wave * 32 * NRB;
     const bool wave_live = wrow0 < rows;
     int32_t my_tok[NRB], my_head[NRB], row_lo[NRB], row_hi[NRB], w_pmin[NRB], w_pmax[NRB];
@@ -501,8 +527,13 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
         my_tok[rb] = row_ok[rb] ? my_row / G : 0;
         my_head[rb] = my_row % G;
         const int32_t my_pos = prefix + my_tok[rb];
-        row_hi[rb] = min(my_pos, hi - 1);
-        row_lo[rb] = (a.window > 0) ? my_pos - a.window + 1 : -(1 << 30);
+        if constexpr (D == 256) {               // the softmax forms the range (FRESH)
+            row_lo[rb] = my_pos;
+            row_hi[rb] = hi - 1;
+        } else {
+            row_hi[rb] = min(my_pos, hi - 1);
+            row_lo[rb] = (a.window > 0) ? my_pos - a.window + 1 : -(1 << 30);
+        }
         // the row block's extreme positions, for the "tile visible to all rows" test
         w_pmin[rb] = prefix + min(n - 1, r0 / G);
         w_pmax[rb] = prefix + min(n - 1, (r0 + 31) / G);
@@ -515,7 +546,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     // page ids of pages page0 + 64c + lane, batch c; missing pages read page 0
     const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
     auto load_ids = [&](int32_t c) -> int32_t {
-        const int32_t pg = page0 + 64 * c + lane;
+        const int32_t pg = page0 + 64 * c + (D == 256 ? lane_id_here() : lane);
         int32_t ph = -1;
         if (pg < a.max_pages) ph = pt[pg];
         if ((uint32_t)ph < (uint32_t)a.num_pages) return ph;
@@ -593,8 +624,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     auto soft_stage_all = [&](int stage, int32_t t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
-            softmax_stage(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], h, a.score_scale,
-                          m_run[rb], l_run[rb], pb[rb][0]);
+            softmax_stage<D == 256>(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], a.window, h,
+                                    a.score_scale, m_run[rb], l_run[rb], pb[rb][0]);
     };
     auto soft_pack_hi = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -782,11 +813,15 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     // (A store with more than 8 bytes of data reads its registers after it
     // issues: the s_nop keeps the next instruction off them.)
     const int32_t n_rows = min(C::ROWS, rows - row0);
+    // D = 256: the group size through an empty asm, so that the division
+    // below forms its reciprocal here instead of keeping the prologue's
+    int32_t Go = G;
+    if constexpr (D == 256) asm volatile("" : "+s"(Go));
     for (int idx = tid; idx < n_rows * (D / 8); idx += C::THREADS) {
         const int r = idx / (D / 8), q = idx % (D / 8);
         const int32_t row = row0 + r;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RB + ((q ^ (r & GM)) << 4));
-        uint16_t* op = a.out + ((int64_t)(q0 + row / G) * a.hq + (int64_t)g * G + row % G) * D + 8 * q;
+        uint16_t* op = a.out + ((int64_t)(q0 + row / Go) * a.hq + (int64_t)g * Go + row % Go) * D + 8 * q;
         asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(op), "v"(v) : "memory");
     }
 }
