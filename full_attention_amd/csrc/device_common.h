@@ -73,6 +73,14 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// acc + lo^2 + hi^2 for the bf16 pair of a word (v_dot2c_f32_bf16: the
+// products are exact in float32, the sum rounds as float32 does).
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_dot;
+__device__ __forceinline__ float sq_sum_bf16x2(uint32_t word, float acc) {
+    const bf16x2_dot v = __builtin_bit_cast(bf16x2_dot, word);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
 __device__ __forceinline__ int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi) {
     return x < lo ? lo : (x > hi ? hi : x);
 }
