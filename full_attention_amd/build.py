@@ -38,7 +38,7 @@ HOSTSAN = ["-O1", "-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=ad
            "-Xarch_host", "-fsanitize=undefined", "-fno-sanitize-recover=undefined"]
 
 SOURCES = ["pakv_api.cpp", "pakv_pool.cpp", "pakv_step.cpp", "kernels_store.hip", "kernels_decode.hip", "kernels_extend.hip",
-           "kernels_extend_general.hip"]
+           "kernels_extend_general.hip", "kernels_extend_stage.hip"]
 
 VARIANTS = {
     None: "libpakv.so",

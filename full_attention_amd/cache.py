@@ -65,6 +65,7 @@ class PagedKVCache:
         self.page_table = None
         self._group_pages = {}     # "sliding" / "full" -> (table tensor, pakv_pages) of that group
         self._workspace = None
+        self._stage_ws = None
 
     def _fill_slab(self, l, s, hkv, d, num_pages, sentinel):
         """Allocates and binds owner layer l's slab, filled with a sentinel
@@ -191,6 +192,22 @@ class PagedKVCache:
             out = torch.empty_like(q)
         pakv.paged_attn_extend_packed(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, k_ext, v_ext, out, nseq,
                                       q.shape[0], max_q_len, max_kv_len, stream)
+        return out
+
+    def extend_staged(self, layer, cu_q, prefix_lens, q, max_q_len, max_kv_len, k_ext=None, v_ext=None, out=None,
+                      stream=None):
+        """Extend on the bf16 MFMA kernel for every format (8-bit slabs, K=V
+        layers and packed chunks staged first into a workspace the cache keeps
+        and grows); k_ext / v_ext as in extend_packed, or None."""
+        nseq = cu_q.shape[0] - 1
+        if out is None:
+            out = torch.empty_like(q)
+        need = pakv.extend_staging_bytes(self.map, layer, nseq, max_q_len, max_kv_len, k_ext is not None)
+        if need and (self._stage_ws is None or self._stage_ws.numel() < need):
+            self._stage_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = self._stage_ws if need else None
+        pakv.paged_attn_extend_staged(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, k_ext, v_ext, out,
+                                      nseq, q.shape[0], max_q_len, max_kv_len, ws, need, stream)
         return out
 
     def capture_decode_step(self, kv_lens, max_kv_len, layers_io, buckets, max_batch=None):

@@ -169,6 +169,12 @@ struct ExtendArgs {
     int32_t window;
     float score_scale;   // sm_scale * log2(e)
     uint32_t* bad_ids;   // counters of a PAKV_DEBUG_BOUNDS build, else null
+    // staged call (the scaled kernel): the slab is the staging workspace of
+    // kernels_extend_stage.hip -- sequence b's pages from its first row's
+    // start at b * stage_stride -- with a key and a value scale per token
+    const float* k_scale;
+    const float* v_scale;
+    int32_t stage_stride;
 };
 
 // XOR key of a kv token's K row in LDS (16-byte granules).  LDS serves a
@@ -312,11 +318,29 @@ struct SoftRow {
 // position - window + 1 on a sliding layer, upper min(position, hi - 1), given
 // as row_hi) and the lane's 8h are formed here, out of values the compiler
 // cannot hoist: kept across the loop they took registers it does not have.
-template <bool FRESH>
+// SC (the staged kernel): sc holds the tile's key scales (tokens 0..31) and
+// value scales (32..63); stage 0 multiplies each score by its key's scale
+// before anything else, and the packing multiplies each weight by its key's
+// value scale (the row sum takes the weights as they are).
+template <bool FRESH, bool SC>
 __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, int32_t t0, bool whole,
                                               int32_t row_lo, int32_t row_hi, int32_t window, int h,
-                                              float score_scale, float& m_run, float& l_run, u32x4& pb0) {
+                                              float score_scale, float& m_run, float& l_run, u32x4& pb0,
+                                              const float* sc) {
     if (stage == 0) {
+        if constexpr (SC) {
+            const int h8 = (lane_id_here() >> 5) << 3;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {           // tokens h8 .. h8 + 7, then 16 + h8 .. + 7
+                const f32x4 k0 = *reinterpret_cast<const f32x4*>(sc + 16 * hf + h8);
+                const f32x4 k1 = *reinterpret_cast<const f32x4*>(sc + 16 * hf + h8 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[8 * hf + e] *= k0[e];
+                    s[8 * hf + 4 + e] *= k1[e];
+                }
+            }
+        }
         if (!whole) {
             // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
             int32_t lo_l, hi_l;
@@ -360,14 +384,35 @@ __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, 
             l_run += s[e];
         }
     } else if (stage == 6) {
-        pb0 = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]), cvt_pk_bf16(s[4], s[5]),
-                    cvt_pk_bf16(s[6], s[7])};
+        if constexpr (SC) {
+            const int h8 = (lane_id_here() >> 5) << 3;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 + h8);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 + h8 + 4);
+            // (a weight of 0 stays 0: a key outside the staged range may
+            // carry any scale)
+            auto w = [](float p, float v) { return p != 0.f ? p * v : 0.f; };
+            pb0 = u32x4{cvt_pk_bf16(w(s[0], v0[0]), w(s[1], v0[1])), cvt_pk_bf16(w(s[2], v0[2]), w(s[3], v0[3])),
+                        cvt_pk_bf16(w(s[4], v1[0]), w(s[5], v1[1])), cvt_pk_bf16(w(s[6], v1[2]), w(s[7], v1[3]))};
+        } else {
+            pb0 = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]), cvt_pk_bf16(s[4], s[5]),
+                        cvt_pk_bf16(s[6], s[7])};
+        }
     }
 }
 constexpr int kSoftStages = 7;
-__device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1) {
-    pb1 = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]), cvt_pk_bf16(s[12], s[13]),
-                cvt_pk_bf16(s[14], s[15])};
+template <bool SC>
+__device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1, const float* sc) {
+    if constexpr (SC) {
+        const int h8 = (lane_id_here() >> 5) << 3;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 48 + h8);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 48 + h8 + 4);
+        auto w = [](float p, float v) { return p != 0.f ? p * v : 0.f; };
+        pb1 = u32x4{cvt_pk_bf16(w(s[8], v0[0]), w(s[9], v0[1])), cvt_pk_bf16(w(s[10], v0[2]), w(s[11], v0[3])),
+                    cvt_pk_bf16(w(s[12], v1[0]), w(s[13], v1[1])), cvt_pk_bf16(w(s[14], v1[2]), w(s[15], v1[3]))};
+    } else {
+        pb1 = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]), cvt_pk_bf16(s[12], s[13]),
+                    cvt_pk_bf16(s[14], s[15])};
+    }
 }
 
 // One wavefront's step of the software pipeline: the score product of tile
@@ -445,11 +490,14 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
     if constexpr (HAVE_S) soft_end();
 }
 
-template <int D>
+// SC: the staged kernel (page ids from the staging layout, per-token scales
+// copied into LDS beside each key tile: 64 floats per tile slot).
+template <int D, bool SC>
 __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel(ExtendArgs a) {
     using C = XCfg<D>;
     constexpr int NRB = C::NRB;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+    constexpr int SC_BYTES = SC ? 2 * 64 * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS + SC_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -545,8 +593,14 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
 
     // page ids of pages page0 + 64c + lane, batch c; missing pages read page 0
     const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+    // staged: sequence b's pages from its first row's start lie at b * stride
+    const int32_t sg_first = SC ? ((a.window > 0) ? max(0, prefix - a.window + 1) : 0) / 16 : 0;
     auto load_ids = [&](int32_t c) -> int32_t {
         const int32_t pg = page0 + 64 * c + (D == 256 ? lane_id_here() : lane);
+        if constexpr (SC) {
+            const int32_t jj = pg - sg_first;
+            return (jj >= 0 && jj < a.stage_stride) ? b * a.stage_stride + jj : 0;
+        }
         int32_t ph = -1;
         if (pg < a.max_pages) ph = pt[pg];
         if ((uint32_t)ph < (uint32_t)a.num_pages) return ph;
@@ -621,15 +675,33 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     SoftRow sr[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) sr[rb].raise = false;
+    // SC: the scale slot (in LDS) of the tile being softmaxed
+    const float* sc_cur = reinterpret_cast<const float*>(lds + C::LDS);
+    auto scale_slot = [&](int32_t tile) {
+        return reinterpret_cast<const float*>(lds + C::LDS + (tile & 1) * 256);
+    };
     auto soft_stage_all = [&](int stage, int32_t t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
-            softmax_stage<D == 256>(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], a.window, h,
-                                    a.score_scale, m_run[rb], l_run[rb], pb[rb][0]);
+            softmax_stage<D == 256, SC>(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], a.window,
+                                        h, a.score_scale, m_run[rb], l_run[rb], pb[rb][0], sc_cur);
     };
     auto soft_pack_hi = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) softmax_pack_hi(s[rb], pb[rb][1]);
+        for (int rb = 0; rb < NRB; ++rb) softmax_pack_hi<SC>(s[rb], pb[rb][1], sc_cur);
+    };
+    // SC: the key and value scales of tile T's pages into its slot (wave 0,
+    // four lanes of 16 bytes per page and kind), copied with the tile's keys
+    auto copy_scales = [&](int32_t T, int32_t pid0, int32_t pid1) {
+        if constexpr (SC) {
+            if (wave == 0 && lane < 4) {
+                const uint32_t dst = lds0 + C::LDS + (T & 1) * 256;
+                dma16_s(a.k_scale + ((int64_t)pid0 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst);
+                dma16_s(a.k_scale + ((int64_t)pid1 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 64);
+                dma16_s(a.v_scale + ((int64_t)pid0 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 128);
+                dma16_s(a.v_scale + ((int64_t)pid1 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 192);
+            }
+        }
     };
     constexpr int kSoftGap = C::KK / 8;
     // the stages fit the value loop, and stage 6 (which overwrites pb[rb][0])
@@ -682,11 +754,13 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
         copy_k_run<D>(k_src + o1, k_voff, kslot(0), 1, wave);
         copy_v_run<D>(v_src + o0, v_voff, vslot(0), 0, wave);
         copy_v_run<D>(v_src + o1, v_voff, vslot(0), 1, wave);
+        copy_scales(0, page_id(0), page_id(1));
         if (n_tiles > 1) {
             ok0 = page_off(page_id(2));
             ok1 = page_off(page_id(3));
             copy_k_run<D>(k_src + ok0, k_voff, kslot(1), 0, wave);
             copy_k_run<D>(k_src + ok1, k_voff, kslot(1), 1, wave);
+            copy_scales(1, page_id(2), page_id(3));
         }
     }
     // Q^T operands, loaded while the first tiles are in flight: lane holds
@@ -734,7 +808,9 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
             slide_ids(2 * t + 4);
             ok0 = page_off(page_id(2 * t + 4));
             ok1 = page_off(page_id(2 * t + 5));
+            copy_scales(t + 2, page_id(2 * t + 4), page_id(2 * t + 5));
         }
+        if constexpr (SC) sc_cur = scale_slot(t + 1);
         const uint32_t vs = vslot(t + 1), ks = kslot(t + 2);
         // copy c of this step: run c / NI (V(t+1) pages 0, 1, then K(t+2) pages 0,
         // 1), copy c % NI of it
@@ -849,16 +925,22 @@ int launch_extend(const ExtendLaunch& s, void* stream) {
     a.group = s.hq / s.hkv;
     a.window = s.window;
     a.score_scale = s.sm_scale * kLog2e;
+    const bool sc = s.stage_stride > 0;          // a staged call: scales beside the staged pages
+    a.k_scale = sc ? s.slab.k_scale : nullptr;
+    a.v_scale = sc ? s.slab.v_scale : nullptr;
+    a.stage_stride = s.stage_stride;
     const int64_t rows = (int64_t)s.max_q_len * a.group;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s.head_dim == 256) {
         using C = XCfg<256>;
         const dim3 grid(s.hkv, (unsigned)((rows + C::ROWS - 1) / C::ROWS), s.num_seqs);
-        launch(PAKV_TIME_EXTEND, extend_kernel<256>, grid, dim3(C::THREADS), 0, st, a);
+        if (sc) launch(PAKV_TIME_EXTEND, extend_kernel<256, true>, grid, dim3(C::THREADS), 0, st, a);
+        else launch(PAKV_TIME_EXTEND, extend_kernel<256, false>, grid, dim3(C::THREADS), 0, st, a);
     } else {
         using C = XCfg<512>;
         const dim3 grid(s.hkv, (unsigned)((rows + C::ROWS - 1) / C::ROWS), s.num_seqs);
-        launch(PAKV_TIME_EXTEND, extend_kernel<512>, grid, dim3(C::THREADS), 0, st, a);
+        if (sc) launch(PAKV_TIME_EXTEND, extend_kernel<512, true>, grid, dim3(C::THREADS), 0, st, a);
+        else launch(PAKV_TIME_EXTEND, extend_kernel<512, false>, grid, dim3(C::THREADS), 0, st, a);
     }
     return (int)hipGetLastError();
 }

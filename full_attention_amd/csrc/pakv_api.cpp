@@ -539,11 +539,21 @@ size_t pakv_decode_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
 
 // Checks shared by the extend calls; k_ext / v_ext: the packed chunk rows (or
 // null: the chunk is read from the slab).
+// Whether a layer's extend needs staging for the bf16 kernel: 8-bit slabs,
+// K=V layers and packed chunks do; a bf16 slab's own chunk does not.
+static bool extend_needs_stage(const pakv_layer_map* map, int32_t layer, bool packed) {
+    const auto& L = map->layers[layer];
+    const auto& S = map->layers[L.source];
+    return packed || L.desc.kv_dtype != PAKV_KV_BF16 || S.desc.k_eq_v;
+}
+
+// workspace (staged calls): null runs the layers that need staging on the
+// general kernel; otherwise they are staged into it for the bf16 kernel
 static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
                                const int32_t* cu_q, const int32_t* prefix_lens, const void* q,
                                const void* k_ext, const void* v_ext, void* out,
                                int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
-                               bool packed, void* stream) {
+                               bool packed, void* stream, void* workspace = nullptr, size_t workspace_bytes = 0) {
     if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
     if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PAKV_OK;
@@ -559,7 +569,14 @@ static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const p
         return fail(PAKV_ERR_INVALID, "k_ext or v_ext is null");
     if (!S.bound) return fail(PAKV_ERR_INVALID, "slab of layer %d (source of %d) is not bound", L.source, layer);
     const int32_t group = L.desc.num_q_heads / L.desc.num_kv_heads;
-    const bool fast = L.desc.kv_dtype == PAKV_KV_BF16 && !S.desc.k_eq_v && !packed;
+    const bool stage = workspace != nullptr && extend_needs_stage(map, layer, packed);
+    const bool fast = stage || (L.desc.kv_dtype == PAKV_KV_BF16 && !S.desc.k_eq_v && !packed);
+    if (stage) {
+        const size_t need = extend_stage_bytes(num_seqs, L.desc.num_kv_heads, L.desc.head_dim, L.desc.window,
+                                               max_q_len, max_kv_len);
+        if (workspace_bytes < need)
+            return fail(PAKV_ERR_WORKSPACE, "workspace of %zu bytes, staging needs %zu", workspace_bytes, need);
+    }
     // grid (Hkv, row blocks of 128 (fast) or 32 (general) (token, head) rows, sequences)
     const int64_t row_blocks = ((int64_t)max_q_len * group + (fast ? 127 : 31)) / (fast ? 128 : 32);
     if (row_blocks > 65535 || num_seqs > 65535)
@@ -587,6 +604,22 @@ static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const p
     a.kv_dtype = L.desc.kv_dtype;
     a.k_eq_v = S.desc.k_eq_v;
     a.v_norm_eps = S.desc.v_norm_eps;
+    if (stage) {
+        if (int e = launch_extend_stage(a, workspace, stream)) return hip_status(e, "paged_attn_extend staging launch");
+        // the bf16 kernel on the staged pages: the workspace is its slab
+        const int32_t stride = extend_stage_stride(L.desc.window, max_q_len, max_kv_len);
+        const int64_t blocks = (int64_t)num_seqs * stride * L.desc.num_kv_heads;
+        auto al = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+        char* w = static_cast<char*>(workspace);
+        const int64_t page_bytes = al(blocks * 16 * L.desc.head_dim * 2);
+        a.slab.k = w;
+        a.slab.v = w + page_bytes;
+        a.slab.k_scale = reinterpret_cast<const float*>(w + 2 * page_bytes);
+        a.slab.v_scale = reinterpret_cast<const float*>(w + 2 * page_bytes + al(blocks * 16 * 4));
+        a.slab.num_pages = (int32_t)((int64_t)num_seqs * stride);
+        a.stage_stride = stride;
+        a.kv_dtype = PAKV_KV_BF16;
+    }
     if (fast) return hip_status(launch_extend(a, stream), "paged_attn_extend launch");
     return hip_status(launch_extend_general(a, stream), "paged_attn_extend launch");
 }
@@ -609,6 +642,29 @@ pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t lay
     clear_error();
     return extend_call(map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q, max_q_len,
                        max_kv_len, true, stream);
+}
+
+size_t pakv_extend_staging_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_q_len,
+                                  int32_t max_kv_len, int32_t packed) {
+    if (!layer_ok(map, layer) || num_seqs <= 0 || max_q_len <= 0 || max_kv_len <= 0) return 0;
+    if (!extend_needs_stage(map, layer, packed != 0)) return 0;
+    const auto& d = map->layers[layer].desc;
+    return extend_stage_bytes(num_seqs, d.num_kv_heads, d.head_dim, d.window, max_q_len, max_kv_len);
+}
+
+pakv_status pakv_paged_attn_extend_staged(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const int32_t* cu_q, const int32_t* prefix_lens,
+                                          const void* q, const void* k_ext, const void* v_ext, void* out,
+                                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+    clear_error();
+    const bool packed = k_ext != nullptr;
+    if (layer_ok(map, layer) && extend_needs_stage(map, layer, packed) && !workspace && num_seqs > 0 &&
+        total_q > 0 && max_q_len > 0)
+        return fail(PAKV_ERR_WORKSPACE, "null workspace: layer %d's extend is staged", layer);
+    return extend_call(map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q, max_q_len,
+                       max_kv_len, packed, stream, workspace, workspace_bytes);
 }
 
 pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream) {

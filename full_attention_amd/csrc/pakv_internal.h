@@ -175,9 +175,18 @@ struct ExtendLaunch {
     int32_t kv_dtype = PAKV_KV_BF16;
     int32_t k_eq_v = 0;
     float v_norm_eps = 0.f;
+    // the bf16 kernel on staged pages (slab = the staging workspace, with
+    // k_scale / v_scale its per-token scales), pages per sequence; 0 otherwise
+    int32_t stage_stride = 0;
 };
-int launch_extend(const ExtendLaunch& a, void* stream);           // bf16 K and V slabs, chunk in the slab
+int launch_extend(const ExtendLaunch& a, void* stream);           // bf16 K and V slabs (or staged pages)
 int launch_extend_general(const ExtendLaunch& a, void* stream);   // 8-bit, K=V, packed chunks
+// staging of a call's visible keys and values for the bf16 kernel
+// (kernels_extend_stage.hip): pages per sequence, workspace bytes, the pass
+int32_t extend_stage_stride(int32_t window, int32_t max_q_len, int32_t max_kv_len);
+size_t extend_stage_bytes(int32_t num_seqs, int32_t hkv, int32_t head_dim, int32_t window, int32_t max_q_len,
+                          int32_t max_kv_len);
+int launch_extend_stage(const ExtendLaunch& a, void* workspace, void* stream);
 
 const char* hip_error_string(int err);
 

@@ -40,7 +40,8 @@ EXPORTED = (
     "pakv_page_pool_table", "pakv_page_pool_free_pages", "pakv_page_pool_released", "pakv_pool_tokens",
     "pakv_decode_step_workspace_bytes", "pakv_decode_step_create", "pakv_decode_step_run",
     "pakv_decode_step_bucket", "pakv_decode_step_destroy", "pakv_set_decode_checks",
-    "pakv_debug_bounds_counts", "pakv_debug_bounds_reset",
+    "pakv_debug_bounds_counts", "pakv_debug_bounds_reset", "pakv_extend_staging_bytes",
+    "pakv_paged_attn_extend_staged",
 )
 
 TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
@@ -117,6 +118,11 @@ lib.pakv_paged_attn_extend.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P
 lib.pakv_paged_attn_extend_packed.restype = _I
 lib.pakv_paged_attn_extend_packed.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                               _P]
+lib.pakv_extend_staging_bytes.restype = _S
+lib.pakv_extend_staging_bytes.argtypes = [_P, _I, _I, _I, _I, _I]
+lib.pakv_paged_attn_extend_staged.restype = _I
+lib.pakv_paged_attn_extend_staged.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                              _P, _S, _P]
 lib.pakv_page_pool_create.restype = _I
 lib.pakv_page_pool_create.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_P)]
 lib.pakv_page_pool_destroy.restype = None
@@ -311,6 +317,18 @@ def paged_attn_extend(layer_map, layer, pages, cu_q, prefix_lens, q, out, num_se
     return _check(lib.pakv_paged_attn_extend(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                              _ptr(prefix_lens), _ptr(q), _ptr(out), num_seqs, total_q,
                                              max_q_len, max_kv_len, _stream(stream)))
+
+
+def extend_staging_bytes(layer_map, layer, num_seqs, max_q_len, max_kv_len, packed):
+    return lib.pakv_extend_staging_bytes(layer_map.handle, layer, num_seqs, max_q_len, max_kv_len, 1 if packed else 0)
+
+
+def paged_attn_extend_staged(layer_map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q,
+                             max_q_len, max_kv_len, workspace, workspace_bytes, stream=None):
+    return _check(lib.pakv_paged_attn_extend_staged(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
+                                                    _ptr(prefix_lens), _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(out),
+                                                    num_seqs, total_q, max_q_len, max_kv_len, _ptr(workspace),
+                                                    workspace_bytes, _stream(stream)))
 
 
 def paged_attn_extend_packed(layer_map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q,

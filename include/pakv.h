@@ -78,7 +78,7 @@ typedef enum {
     PAKV_ERR_INVALID = 1,     /* a null pointer, a negative size, an index out of range */
     PAKV_ERR_UNSUPPORTED = 2, /* a shape this build has no kernel for (head_dim, group size, page size) */
     PAKV_ERR_ALIAS = 3,       /* a KV-sharing rule is broken (see pakv_layer_map_create) */
-    PAKV_ERR_WORKSPACE = 4,   /* decode workspace missing or too small */
+    PAKV_ERR_WORKSPACE = 4,   /* decode or staging workspace missing or too small */
     PAKV_ERR_HIP = 5          /* the HIP runtime reported an error; the message carries its text */
 } pakv_status;
 
@@ -346,6 +346,36 @@ pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t lay
                                           const void* q, const void* k_ext, const void* v_ext, void* out,
                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, void* stream);
+
+/* Chunked prefill for every format on the bf16 MFMA kernel.  8-bit slabs, K=V
+ * layers and packed chunks (which pakv_paged_attn_extend and _packed run on a
+ * kernel that stages each tile itself) are first staged into `workspace` by
+ * one pass: for every page of the call's visible key range, the keys as bf16
+ * codes (8-bit codes exactly; packed rows as given), the values as bf16
+ * dim-major pages (a K=V layer's values are its key rows), and per token a key
+ * scale and a value scale (the format's scales; 1 for packed rows; a K=V
+ * layer's value scale 1 / sqrt(mean square + eps), unsloth commit 749fb75).
+ * The bf16 kernel then reads the staged pages, multiplying each score by its
+ * key's scale and each weight by its key's value scale: the arithmetic of the
+ * other extend calls, exact codes with float32 scales.  A bf16 layer's own
+ * chunk (k_ext NULL) needs no staging and runs as in pakv_paged_attn_extend.
+ *   k_ext, v_ext : NULL (the chunk is read from the slab, as in
+ *                  pakv_paged_attn_extend), or the packed chunk rows as in
+ *                  pakv_paged_attn_extend_packed
+ *   workspace    : device memory of at least pakv_extend_staging_bytes(...,
+ *                  packed = k_ext != NULL) bytes (0: none needed; may then be
+ *                  NULL); any content; overwritten by the call; calls that
+ *                  may overlap need separate workspaces
+ * Other arguments as in pakv_paged_attn_extend.  Errors: PAKV_ERR_WORKSPACE for
+ * a missing or short workspace, else as pakv_paged_attn_extend. */
+size_t pakv_extend_staging_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_q_len,
+                                 int32_t max_kv_len, int32_t packed);
+pakv_status pakv_paged_attn_extend_staged(const pakv_layer_map* map, int32_t layer, const pakv_pages* pages,
+                                          const int32_t* cu_q, const int32_t* prefix_lens,
+                                          const void* q, const void* k_ext, const void* v_ext, void* out,
+                                          int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* ---- Decode step graphs ---------------------------------------------------------
  * A whole decode step of a layer stack, captured once per batch-size bucket

@@ -176,6 +176,44 @@ def test_argument_errors_are_returned_before_launch():
                                    2, 5, None) == pakv.ERR_INVALID
 
 
+def test_extend_staging_sizes_and_refusals():
+    """The staged extend's workspace: none for a bf16 layer's own chunk; for
+    8-bit layers and packed chunks, two bf16 page sets and two scale arrays
+    over the pages a chunk's rows see (whole context on a full layer, window
+    plus chunk on a sliding one); a missing or short workspace is refused
+    before any launch."""
+    m = _bound_map()
+    assert pakv.extend_staging_bytes(m, 0, 2, 5, 40, False) == 0        # bf16, chunk from the slab
+    assert pakv.extend_staging_bytes(m, 1, 2, 5, 40, False) == 0        # shared bf16
+    al = lambda x: (x + 255) // 256 * 256
+    for packed in (False, True):
+        blocks = 2 * ((40 + 15) // 16 + 1) * 1
+        want = 2 * al(blocks * 16 * 256 * 2) + 2 * al(blocks * 16 * 4)
+        assert pakv.extend_staging_bytes(m, 2, 2, 5, 40, packed) == want
+    blocks = 2 * ((40 + 15) // 16 + 1)
+    assert pakv.extend_staging_bytes(m, 0, 2, 5, 40, True) == 2 * al(blocks * 16 * 512) + 2 * al(blocks * 64)
+    ms = pakv.LayerMap([_desc(w=512, dtype=pakv.KV_INT8_PTH)])
+    span = lambda q, kv: pakv.extend_staging_bytes(ms, 0, 1, q, kv, False)
+    assert span(64, 8192) == span(64, 4096) < span(64, 576)  * 10          # window + chunk, not the context
+    assert span(64, 100) < span(64, 8192)
+    assert pakv.extend_staging_bytes(m, 7, 2, 5, 40, False) == 0        # bad layer
+    assert pakv.extend_staging_bytes(m, 2, 0, 5, 40, False) == 0        # nothing to stage
+    pages = pakv.Pages(0x5000, 2, 4)
+    lib = pakv.lib
+    need = pakv.extend_staging_bytes(m, 2, 2, 5, 40, False)
+    assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, None, None,
+                                             0x7000, 2, 10, 5, 40, None, 0, None) == pakv.ERR_WORKSPACE
+    assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, None, None,
+                                             0x7000, 2, 10, 5, 40, 0x9000, need - 1, None) == pakv.ERR_WORKSPACE
+    assert "staging" in pakv.last_error()
+    # packed on a bf16 layer needs staging too; without its value rows it is refused
+    assert lib.pakv_paged_attn_extend_staged(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x6300, None,
+                                             0x7000, 2, 10, 5, 40, 0x9000, 1 << 30, None) == pakv.ERR_INVALID
+    # empty chunk: nothing to do, no workspace needed
+    assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), None, None, None, None, None,
+                                             None, 2, 0, 0, 40, None, 0, None) == pakv.OK
+
+
 def test_unbound_source_slab_is_an_error():
     m = pakv.LayerMap([_desc(), _desc(src=0)])
     pages = pakv.Pages(0x5000, 1, 4)
