@@ -168,19 +168,46 @@ struct ExtendArgs {
     int32_t group;
     int32_t window;
     float score_scale;   // sm_scale * log2(e)
+    float inv_group;     // 1 / group, as a float
     uint32_t* bad_ids;   // counters of a PAKV_DEBUG_BOUNDS build, else null
     // staged call (the scaled kernel): the slab is the staging workspace of
-    // kernels_extend_stage.hip -- sequence b's pages from its first row's
-    // start at b * stage_stride -- with a key and a value scale per token
-    const float* k_scale;
-    const float* v_scale;
+    // kernels_extend_stage.hip -- sequence b's pages from the tile of its
+    // first row's start at b * stage_stride, stage_pages in all -- and
+    // stage_scales holds per (KV head, page) the 16 key scales then the 16
+    // value scales of its tokens, [Hkv][stage_pages][32] floats
+    const float* stage_scales;
     int32_t stage_stride;
+    int32_t stage_pages;
 };
 
 // XOR key of a kv token's K row in LDS (16-byte granules).  LDS serves a
 // 16-byte-per-lane read 16 lanes at a time over 64 banks; the 16 rows that 16
 // consecutive lanes read land in 16 different bank groups.
 __device__ __forceinline__ int k_swz(int tk) { return tk & 15; }
+
+// LDS byte offsets, within a K tile slot, of the 16 bytes a lane reads at
+// score step kk: granule 2 kk + h of its K row tk, XOR the row's key.  With
+// base = tk * row bytes + ((h ^ key) * 16), granule 16 c + 8 a + 2 b + h
+// (kk = 8 c + 4 a + b) lies at base ^ ((8 a + 2 b) * 16), plus 256 c: the
+// key and 8 a + 2 b + h only touch bits 4..7, and h is their bit 4.  At
+// D = 256 (two wavefronts per SIMD, registers short) the offset is formed at
+// each read from the base; at D = 512 (one wavefront per SIMD, whose own
+// VALU work is not hidden) the 8 XORed offsets are kept.
+template <int D>
+struct KOffsets {
+    static constexpr int N = (D == 256) ? 1 : 8;
+    int v[N];
+    __device__ __forceinline__ void init(int base) {
+        if constexpr (N == 1) v[0] = base;
+        else
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) v[s8] = base ^ ((8 * (s8 >> 2) + 2 * (s8 & 3)) * 16);
+    }
+    __device__ __forceinline__ int operator()(int kk) const {
+        if constexpr (N == 1) return (v[0] ^ ((8 * ((kk >> 2) & 1) + 2 * (kk & 3)) * 16)) + (kk >> 3) * 256;
+        else return v[((kk >> 2) & 1) * 4 + (kk & 3)] + (kk >> 3) * 256;
+    }
+};
 
 template <int D>
 struct XCfg {
@@ -314,26 +341,30 @@ struct SoftRow {
 };
 
 // The row's visible kv range is [row_lo, row_hi].  FRESH (the D = 256
-// kernel): row_lo holds the row's position instead, and the range (lower end
-// position - window + 1 on a sliding layer, upper min(position, hi - 1), given
-// as row_hi) and the lane's 8h are formed here, out of values the compiler
-// cannot hoist: kept across the loop they took registers it does not have.
-// SC (the staged kernel): sc holds the tile's key scales (tokens 0..31) and
-// value scales (32..63); stage 0 multiplies each score by its key's scale
+// kernel): the row's position, the range (lower end position - window + 1 on
+// a sliding layer, upper min(position, hi - 1), given as row_hi) and the
+// lane's 8h are formed here, out of values the compiler cannot hoist: kept
+// across the loop they took registers it does not have.  The position is
+// row_lo + floor((row_r + col) / G) for the lane's column col, with the
+// wave-uniform row_lo (prefix + first row / G), row_r (first row mod G) and
+// inv_g = 1 / G: (x + 1/2) / G lies at least 1/(2G) from an integer, far
+// beyond the float product's error, so the floor is exact.
+// SC (the staged kernel): sc holds the tile's scales, per page the 16 key
+// scales then the 16 value scales of its tokens; stage 0 multiplies each score by its key's scale
 // before anything else, and the packing multiplies each weight by its key's
 // value scale (the row sum takes the weights as they are).
 template <bool FRESH, bool SC>
 __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, int32_t t0, bool whole,
                                               int32_t row_lo, int32_t row_hi, int32_t window, int h,
                                               float score_scale, float& m_run, float& l_run, u32x4& pb0,
-                                              const float* sc) {
+                                              const float* sc, int32_t row_r, float inv_g) {
     if (stage == 0) {
         if constexpr (SC) {
             const int h8 = (lane_id_here() >> 5) << 3;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {           // tokens h8 .. h8 + 7, then 16 + h8 .. + 7
-                const f32x4 k0 = *reinterpret_cast<const f32x4*>(sc + 16 * hf + h8);
-                const f32x4 k1 = *reinterpret_cast<const f32x4*>(sc + 16 * hf + h8 + 4);
+                const f32x4 k0 = *reinterpret_cast<const f32x4*>(sc + 32 * hf + h8);
+                const f32x4 k1 = *reinterpret_cast<const f32x4*>(sc + 32 * hf + h8 + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     s[8 * hf + e] *= k0[e];
@@ -345,9 +376,9 @@ __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, 
             // element e holds kv offset 8h + e + 8 (e >= 8) of the tile
             int32_t lo_l, hi_l;
             if constexpr (FRESH) {
-                const int32_t h8 = (lane_id_here() >> 5) << 3;
-                int32_t pos = row_lo;
-                asm volatile("" : "+v"(pos));
+                const int32_t lid = lane_id_here();
+                const int32_t h8 = (lid >> 5) << 3;
+                const int32_t pos = row_lo + (int32_t)(((float)(row_r + (lid & 31)) + 0.5f) * inv_g);
                 lo_l = (window > 0 ? pos - window + 1 : -(1 << 30)) - t0 - h8;
                 hi_l = min(pos, row_hi) - t0 - h8;
             } else {
@@ -386,8 +417,8 @@ __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, 
     } else if (stage == 6) {
         if constexpr (SC) {
             const int h8 = (lane_id_here() >> 5) << 3;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 + h8);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 + h8 + 4);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 16 + h8);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 16 + h8 + 4);
             // (a weight of 0 stays 0: a key outside the staged range may
             // carry any scale)
             auto w = [](float p, float v) { return p != 0.f ? p * v : 0.f; };
@@ -431,7 +462,7 @@ __device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1, con
 // of it, so issued together they stall the matrix work.  With HAVE_S = false
 // only the value product runs (the last tile).
 template <int D, bool HAVE_S, typename Copy, typename Soft, typename SoftEnd>
-__device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const int (&k_off)[8], int v_off,
+__device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, const KOffsets<D>& k_off, int v_off,
                                           const u32x4 (&qreg)[XCfg<D>::NRB][D / 16],
                                           const u32x4 (&pb)[XCfg<D>::NRB][2], f32x16 (&s)[XCfg<D>::NRB],
                                           f32x16 (&o)[XCfg<D>::OT], int n_copies, Copy copy, Soft soft, SoftEnd soft_end) {
@@ -445,10 +476,8 @@ __device__ __forceinline__ void step_mfma(const uint8_t* kb, const uint8_t* vb, 
             if (e / kCopyGap < n_copies) copy(e / kCopyGap);
         }
     };
-    // score step i: granules 2i + h of the lane's K row, at k_off[bits 2, 1..0 of i] + 256 (i / 8)
-    auto ld_k = [&](int i) {
-        return *reinterpret_cast<const u32x4*>(kb + k_off[((i >> 2) & 1) * 4 + (i & 3)] + (i >> 3) * 256);
-    };
+    // score step i: granules 2i + h of the lane's K row
+    auto ld_k = [&](int i) { return *reinterpret_cast<const u32x4*>(kb + k_off(i)); };
     // value step i: kv half st = i / MT, output tile m = i % MT
     auto ld_v = [&](int i) {
         return *reinterpret_cast<const u32x4*>(vb + (i / MT) * (16 * D * 2) + (i % MT) * 1024 + v_off);
@@ -565,7 +594,8 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
     // the softmax forms the range); a row block past the chunk is idle
     const int32_t wrow0 = row0 + wave * 32 * NRB;
     const bool wave_live = wrow0 < rows;
-    int32_t my_tok[NRB], my_head[NRB], row_lo[NRB], row_hi[NRB], w_pmin[NRB], w_pmax[NRB];
+    int32_t my_tok[NRB], my_head[NRB], row_lo[NRB], row_hi[NRB], row_r[NRB], w_pmin[NRB], w_pmax[NRB];
+    const float inv_g = a.inv_group;
     bool row_ok[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -576,11 +606,13 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
         my_head[rb] = my_row % G;
         const int32_t my_pos = prefix + my_tok[rb];
         if constexpr (D == 256) {               // the softmax forms the range (FRESH)
-            row_lo[rb] = my_pos;
+            row_lo[rb] = prefix + r0 / G;
+            row_r[rb] = r0 % G;
             row_hi[rb] = hi - 1;
         } else {
             row_hi[rb] = min(my_pos, hi - 1);
             row_lo[rb] = (a.window > 0) ? my_pos - a.window + 1 : -(1 << 30);
+            row_r[rb] = 0;
         }
         // the row block's extreme positions, for the "tile visible to all rows" test
         w_pmin[rb] = prefix + min(n - 1, r0 / G);
@@ -593,8 +625,9 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
 
     // page ids of pages page0 + 64c + lane, batch c; missing pages read page 0
     const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-    // staged: sequence b's pages from its first row's start lie at b * stride
-    const int32_t sg_first = SC ? ((a.window > 0) ? max(0, prefix - a.window + 1) : 0) / 16 : 0;
+    // staged: sequence b's pages from the tile of its first row's start lie
+    // at b * stride (an even count, so a tile's two pages are neighbours)
+    const int32_t sg_first = SC ? 2 * (((a.window > 0) ? max(0, prefix - a.window + 1) : 0) / kTile) : 0;
     auto load_ids = [&](int32_t c) -> int32_t {
         const int32_t pg = page0 + 64 * c + (D == 256 ? lane_id_here() : lane);
         if constexpr (SC) {
@@ -638,14 +671,11 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
 
     // LDS offsets this lane reads: K row tau(col), granules (2 kk + h) ^ key;
     // the key has four bits, so it moves a granule within its group of 16
-    // (k_off[a * 4 + b] serves kk = 8c + 4a + b, plus 256c bytes)
-    int k_off[8];
+    KOffsets<D> k_off;
     {
         const int j = col >> 3, hh = (col >> 2) & 1, i = col & 3;
         const int tk = 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8)
-            k_off[s8] = tk * C::KROW + (((8 * (s8 >> 2) + 2 * (s8 & 3) + h) ^ k_swz(tk)) * 16);
+        k_off.init(tk * C::KROW + ((h ^ k_swz(tk)) * 16));
     }
     const int v_off = col * 32 + ((h ^ ((col >> 3) & 1)) * 16);
 
@@ -684,23 +714,21 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
             softmax_stage<D == 256, SC>(stage, s[rb], sr[rb], t0, is_whole(t0, rb), row_lo[rb], row_hi[rb], a.window,
-                                        h, a.score_scale, m_run[rb], l_run[rb], pb[rb][0], sc_cur);
+                                        h, a.score_scale, m_run[rb], l_run[rb], pb[rb][0], sc_cur, row_r[rb], inv_g);
     };
     auto soft_pack_hi = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) softmax_pack_hi<SC>(s[rb], pb[rb][1], sc_cur);
     };
-    // SC: the key and value scales of tile T's pages into its slot (wave 0,
-    // four lanes of 16 bytes per page and kind), copied with the tile's keys
-    auto copy_scales = [&](int32_t T, int32_t pid0, int32_t pid1) {
+    // SC: the scales of tile T's pages into its slot, copied with the tile's
+    // keys: its second page is its first's neighbour in the staging layout
+    // (staged tiles are whole), so one 256-byte copy by wave 0's first 16
+    // lanes.  (A tile past the staged range reads page 0's: masked.)
+    auto copy_scales = [&](int32_t T, int32_t pid0) {
         if constexpr (SC) {
-            if (wave == 0 && lane < 4) {
-                const uint32_t dst = lds0 + C::LDS + (T & 1) * 256;
-                dma16_s(a.k_scale + ((int64_t)pid0 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst);
-                dma16_s(a.k_scale + ((int64_t)pid1 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 64);
-                dma16_s(a.v_scale + ((int64_t)pid0 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 128);
-                dma16_s(a.v_scale + ((int64_t)pid1 * a.hkv + g) * 16, (uint32_t)(lane * 16), dst + 192);
-            }
+            if (wave == 0 && lane < 16)
+                dma16_s(a.stage_scales + ((int64_t)g * a.stage_pages + pid0) * 32, (uint32_t)(lane * 16),
+                        lds0 + C::LDS + (T & 1) * 256);
         }
     };
     constexpr int kSoftGap = C::KK / 8;
@@ -754,13 +782,13 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
         copy_k_run<D>(k_src + o1, k_voff, kslot(0), 1, wave);
         copy_v_run<D>(v_src + o0, v_voff, vslot(0), 0, wave);
         copy_v_run<D>(v_src + o1, v_voff, vslot(0), 1, wave);
-        copy_scales(0, page_id(0), page_id(1));
+        copy_scales(0, page_id(0));
         if (n_tiles > 1) {
             ok0 = page_off(page_id(2));
             ok1 = page_off(page_id(3));
             copy_k_run<D>(k_src + ok0, k_voff, kslot(1), 0, wave);
             copy_k_run<D>(k_src + ok1, k_voff, kslot(1), 1, wave);
-            copy_scales(1, page_id(2), page_id(3));
+            copy_scales(1, page_id(2));
         }
     }
     // Q^T operands, loaded while the first tiles are in flight: lane holds
@@ -779,12 +807,10 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
             const uint8_t* kbuf = lds + 0;
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                s[rb] = asm_mfma_first(*reinterpret_cast<const u32x4*>(kbuf + k_off[0]), qreg[rb][0]);
+                s[rb] = asm_mfma_first(*reinterpret_cast<const u32x4*>(kbuf + k_off(0)), qreg[rb][0]);
 #pragma unroll
                 for (int kk = 1; kk < C::KK; ++kk)
-                    asm_mfma_acc(s[rb], *reinterpret_cast<const u32x4*>(kbuf + k_off[((kk >> 2) & 1) * 4 + (kk & 3)] +
-                                                                        (kk >> 3) * 256),
-                                 qreg[rb][kk]);
+                    asm_mfma_acc(s[rb], *reinterpret_cast<const u32x4*>(kbuf + k_off(kk)), qreg[rb][kk]);
                 asm_mfma_drain(s[rb]);
             }
 #pragma unroll
@@ -808,7 +834,7 @@ __global__ __launch_bounds__(XCfg<D>::THREADS, XCfg<D>::MINB) void extend_kernel
             slide_ids(2 * t + 4);
             ok0 = page_off(page_id(2 * t + 4));
             ok1 = page_off(page_id(2 * t + 5));
-            copy_scales(t + 2, page_id(2 * t + 4), page_id(2 * t + 5));
+            copy_scales(t + 2, page_id(2 * t + 4));
         }
         if constexpr (SC) sc_cur = scale_slot(t + 1);
         const uint32_t vs = vslot(t + 1), ks = kslot(t + 2);
@@ -925,10 +951,11 @@ int launch_extend(const ExtendLaunch& s, void* stream) {
     a.group = s.hq / s.hkv;
     a.window = s.window;
     a.score_scale = s.sm_scale * kLog2e;
+    a.inv_group = 1.0f / (float)a.group;
     const bool sc = s.stage_stride > 0;          // a staged call: scales beside the staged pages
-    a.k_scale = sc ? s.slab.k_scale : nullptr;
-    a.v_scale = sc ? s.slab.v_scale : nullptr;
+    a.stage_scales = sc ? s.slab.k_scale : nullptr;
     a.stage_stride = s.stage_stride;
+    a.stage_pages = sc ? s.slab.num_pages : 0;
     const int64_t rows = (int64_t)s.max_q_len * a.group;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s.head_dim == 256) {

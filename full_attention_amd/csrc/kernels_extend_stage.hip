@@ -22,9 +22,12 @@
 //     zeros with zero scales, so a never-written slot (possibly NaN) never
 //     reaches the arithmetic.
 // Layout: sequence b's staged pages are workspace pages b * stride + j, page
-// j holding positions 16 (lo_b / 16 + j) .. + 15, where lo_b is the first
-// position its first row sees (0 on a full layer); blocks (page, KV head) as
-// in a slab.
+// j holding positions 16 (2 (lo_b / 32) + j) .. + 15, where lo_b is the first
+// position its first row sees (0 on a full layer): whole 32-key tiles of the
+// bf16 kernel, so a tile's two pages are neighbours (stride is even).  K and
+// V blocks (page, KV head) as in a slab; the scales per (KV head, page), the
+// 16 key scales then the 16 value scales of its tokens, so that a tile's are
+// 256 contiguous bytes.
 
 #include <algorithm>
 
@@ -57,8 +60,7 @@ struct StageArgs {
     float v_norm_eps;
     uint16_t* sk;               // staged K pages  [B * stride][Hkv][16][D]
     uint16_t* sv;               // staged V pages  [B * stride][Hkv][D][16]
-    float* sks;                 // key scales      [B * stride][Hkv][16]
-    float* svs;                 // value scales    [B * stride][Hkv][16]
+    float* ssc;                 // scales          [Hkv][B * stride][32]: 16 key, 16 value
     uint32_t* bad_ids;          // counters of a PAKV_DEBUG_BOUNDS build, else null
 };
 
@@ -88,10 +90,11 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
     const int32_t P = a.prefix_lens[b];
     const int32_t hi = min(P + n, a.max_kv_len);                          // the last row's end
     const int32_t lo = (a.window > 0) ? max(0, P - a.window + 1) : 0;     // the first row's start
-    const int32_t pg = lo / 16 + j;
+    const int32_t pg = 2 * (lo / 32) + j;
     if (16 * pg >= hi) return;                   // past every row's range: never read
     const bool packed = a.k_ext != nullptr;
     const int64_t sblk = ((int64_t)b * a.stride + j) * a.hkv + g;
+    float* ssc = a.ssc + ((int64_t)g * gridDim.z * a.stride + (int64_t)b * a.stride + j) * 32;
 
     // the slab block of this page (read only for live tokens below the chunk
     // when packed); an id outside the pool reads page 0, as the kernels do
@@ -149,8 +152,8 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
                 }
                 if constexpr (F == kFmtKEQV) vs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.v_norm_eps);
             }
-            a.sks[sblk * 16 + tt] = ks;
-            a.svs[sblk * 16 + tt] = vs;
+            ssc[tt] = ks;
+            ssc[16 + tt] = vs;
         }
     }
     // packed value rows of the page, token-major, for the transpose below
@@ -217,18 +220,20 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
 
 namespace pakv {
 
-// Staged pages per sequence: enough for the positions any row of a chunk of
-// at most max_q_len tokens sees, from its first row's start.
+// Staged pages per sequence: the whole 32-key tiles holding the positions any
+// row of a chunk of at most max_q_len tokens sees (at most span of them, from
+// the first row's start; the first tile may begin 31 positions earlier).
 int32_t extend_stage_stride(int32_t window, int32_t max_q_len, int32_t max_kv_len) {
     const int64_t span = window > 0 ? std::min<int64_t>((int64_t)window + max_q_len, max_kv_len) : max_kv_len;
-    return (int32_t)((span + 15) / 16 + 1);
+    return (int32_t)(2 * ((span + 30) / 32 + 1));
 }
 
 size_t extend_stage_bytes(int32_t num_seqs, int32_t hkv, int32_t head_dim, int32_t window, int32_t max_q_len,
                           int32_t max_kv_len) {
     const int64_t blocks = (int64_t)num_seqs * extend_stage_stride(window, max_q_len, max_kv_len) * hkv;
     auto al = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
-    return (size_t)(2 * al(blocks * 16 * head_dim * 2) + 2 * al(blocks * 16 * 4));
+    // (one spare block of scales: a copy of a tile's two pages stays inside)
+    return (size_t)(2 * al(blocks * 16 * head_dim * 2) + al((blocks + 1) * 32 * 4));
 }
 
 int launch_extend_stage(const ExtendLaunch& s, void* workspace, void* stream) {
@@ -257,9 +262,7 @@ int launch_extend_stage(const ExtendLaunch& s, void* workspace, void* stream) {
     w += al(blocks * 16 * s.head_dim * 2);
     a.sv = reinterpret_cast<uint16_t*>(w);
     w += al(blocks * 16 * s.head_dim * 2);
-    a.sks = reinterpret_cast<float*>(w);
-    w += al(blocks * 16 * 4);
-    a.svs = reinterpret_cast<float*>(w);
+    a.ssc = reinterpret_cast<float*>(w);
     a.bad_ids = debug_bad_ids_ptr();
     const int f = s.k_eq_v ? kFmtKEQV
                            : (s.kv_dtype == PAKV_KV_INT8_PTH ? kFmtINT8 : (s.kv_dtype == PAKV_KV_FP8_PTH ? kFmtFP8 : kFmtBF16));

@@ -614,8 +614,8 @@ static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const p
         const int64_t page_bytes = al(blocks * 16 * L.desc.head_dim * 2);
         a.slab.k = w;
         a.slab.v = w + page_bytes;
-        a.slab.k_scale = reinterpret_cast<const float*>(w + 2 * page_bytes);
-        a.slab.v_scale = reinterpret_cast<const float*>(w + 2 * page_bytes + al(blocks * 16 * 4));
+        a.slab.k_scale = reinterpret_cast<const float*>(w + 2 * page_bytes);   // [Hkv][pages][32]
+        a.slab.v_scale = nullptr;
         a.slab.num_pages = (int32_t)((int64_t)num_seqs * stride);
         a.stage_stride = stride;
         a.kv_dtype = PAKV_KV_BF16;

@@ -186,15 +186,15 @@ def test_extend_staging_sizes_and_refusals():
     assert pakv.extend_staging_bytes(m, 0, 2, 5, 40, False) == 0        # bf16, chunk from the slab
     assert pakv.extend_staging_bytes(m, 1, 2, 5, 40, False) == 0        # shared bf16
     al = lambda x: (x + 255) // 256 * 256
+    stride = 2 * ((40 + 30) // 32 + 1)          # whole 32-key tiles over 40 positions, one more for the start
+    blocks = 2 * stride * 1
     for packed in (False, True):
-        blocks = 2 * ((40 + 15) // 16 + 1) * 1
-        want = 2 * al(blocks * 16 * 256 * 2) + 2 * al(blocks * 16 * 4)
+        want = 2 * al(blocks * 16 * 256 * 2) + al((blocks + 1) * 32 * 4)
         assert pakv.extend_staging_bytes(m, 2, 2, 5, 40, packed) == want
-    blocks = 2 * ((40 + 15) // 16 + 1)
-    assert pakv.extend_staging_bytes(m, 0, 2, 5, 40, True) == 2 * al(blocks * 16 * 512) + 2 * al(blocks * 64)
+    assert pakv.extend_staging_bytes(m, 0, 2, 5, 40, True) == 2 * al(blocks * 16 * 512) + al((blocks + 1) * 128)
     ms = pakv.LayerMap([_desc(w=512, dtype=pakv.KV_INT8_PTH)])
     span = lambda q, kv: pakv.extend_staging_bytes(ms, 0, 1, q, kv, False)
-    assert span(64, 8192) == span(64, 4096) < span(64, 576)  * 10          # window + chunk, not the context
+    assert span(64, 8192) == span(64, 4096) < span(64, 576) * 10           # window + chunk, not the context
     assert span(64, 100) < span(64, 8192)
     assert pakv.extend_staging_bytes(m, 7, 2, 5, 40, False) == 0        # bad layer
     assert pakv.extend_staging_bytes(m, 2, 0, 5, 40, False) == 0        # nothing to stage
