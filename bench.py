@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch the decode steps eagerly instead of from graphs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["e2b", "26b", "int8", "extend"], default=None,
+    ap.add_argument("--only", choices=["e2b", "26b", "int8", "extend", "extend_int8"], default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--no-ladder", action="store_true",
                     help="skip the per-batch-bucket step times (profiling runs: every dispatch is then one of "
@@ -413,11 +413,16 @@ def decode_report(torch, pakv, st, args, wl_name, config):
 
 # ------------------------------------------------------------------ extend workload
 
-def setup_extend(torch):
+def setup_extend(torch, kv_dtype="bf16"):
+    """The E2B-like extend stack; kv_dtype other than bf16 gives every layer
+    that slab format, and its extend calls go through the staged path."""
+    import dataclasses
     from full_attention_amd.cache import PagedKVCache
     from workloads import DeviceDraws, e2b_extend_workload, make_page_pool
 
     wl = e2b_extend_workload()
+    if kv_dtype != "bf16":
+        wl = dataclasses.replace(wl, layers=[dataclasses.replace(s, kv_dtype=kv_dtype) for s in wl.layers])
     P = np.array(wl.cached_lens, dtype=np.int64)
     n = np.array(wl.extend_lens, dtype=np.int64)
     B = len(P)
@@ -444,14 +449,27 @@ def setup_extend(torch):
     for s in layers:
         q.append(draws.bf16((int(cu_n[-1]), s.num_q_heads, s.head_dim)))
         out.append(torch.empty_like(q[-1]))
+    # staged: one workspace per source layer; a KV-shared layer reuses what
+    # its source's call staged (same slab, pages and lengths)
+    stage_ws = {}
+    if kv_dtype != "bf16":
+        for l in owners:
+            need = cache.staging_bytes(l, B, int(n.max()), int((P + n).max()))
+            stage_ws[l] = torch.empty(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
-    return dict(wl=wl, cache=cache, layers=layers, owners=owners, B=B, P=P, n=n,
+    return dict(wl=wl, cache=cache, layers=layers, owners=owners, B=B, P=P, n=n, staged=kv_dtype != "bf16",
+                stage_ws=stage_ws,
                 cu_t=i32(torch, cu_n), P_t=i32(torch, P), chunk_k=chunk_k, chunk_v=chunk_v, q=q, out=out,
                 max_q=int(n.max()), max_kv=int((P + n).max()))
 
 
 def extend_layer(st, l):
-    st["cache"].extend(l, st["cu_t"], st["P_t"], st["q"][l], st["max_q"], st["max_kv"], out=st["out"][l])
+    if st["staged"]:
+        src = st["cache"].sources[l]
+        st["cache"].extend_staged(l, st["cu_t"], st["P_t"], st["q"][l], st["max_q"], st["max_kv"], out=st["out"][l],
+                                  workspace=st["stage_ws"][src], stage=src == l)
+    else:
+        st["cache"].extend(l, st["cu_t"], st["P_t"], st["q"][l], st["max_q"], st["max_kv"], out=st["out"][l])
 
 
 def extend_step(st):
@@ -475,8 +493,9 @@ def extend_flops(st):
     return out
 
 
-def extend_report(torch, pakv, args):
-    ex = setup_extend(torch)
+def extend_report(torch, pakv, args, kv_dtype="bf16"):
+    ex = setup_extend(torch, kv_dtype)
+    tag = ",staged" if ex["staged"] else ""
     nl = len(ex["layers"])
     extend_step(ex)
     torch.cuda.synchronize()
@@ -490,7 +509,7 @@ def extend_report(torch, pakv, args):
     mean_ex, emethod = kernel_durations(torch, pakv, lambda: extend_step(ex), nl, pakv.TIME_EXTEND, 1)
     eg = {}
     for l, s in enumerate(ex["layers"]):
-        key = f"extend_kernel<{s.head_dim}>"
+        key = f"extend_kernel<{s.head_dim}{tag}>"
         g = eg.setdefault(key, {"ms": 0.0, "launches": 0, "flops": 0})
         g["ms"] += float(mean_ex[l])
         g["launches"] += 1
@@ -500,20 +519,28 @@ def extend_report(torch, pakv, args):
     rep = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_ex, 3),
            "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
            "config": {"workload": EXTEND_WL + ", prefixes 0/1024/2048/4096, "
-                                  "2048-token chunks stored on the 15 owners", "flops_per_step": int(sum(flops)),
-                      "launch": "eager (store then extend per layer)"},
+                                  "2048-token chunks stored on the 15 owners"
+                                  + (f", {kv_dtype} per-token-head KV on every layer, extend staged"
+                                     if ex["staged"] else ""), "flops_per_step": int(sum(flops)),
+                      "launch": "eager (store then extend per layer)"
+                                + (": staging pass + bf16 MFMA kernel per extend call" if ex["staged"] else "")},
            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "traffic": load_traffic(en, EXTEND_WL, source_hash(*EXTEND_SOURCES)),
+                        "traffic": None if ex["staged"] else load_traffic(en, EXTEND_WL,
+                                                                          source_hash(*EXTEND_SOURCES)),
                         "kernel": en, "launches_per_step": e["launches"], "timing": emethod,
                         "mean_launch_us": round(e["ms"] / e["launches"] * 1e3, 1),
                         "algorithmic_flops_per_launch": int(e["flops"] / e["launches"]),
                         "per_kernel_us_per_step": {k: round(v["ms"] * 1e3, 1) for k, v in eg.items()}}}
-    if not args.no_cold:
+    if ex["staged"]:
+        mean_st, _ = kernel_durations(torch, pakv, lambda: extend_step(ex), len(ex["owners"]), pakv.TIME_STAGE, 1)
+        rep["staging_us_per_step"] = round(float(np.sum(mean_st)) * 1e3, 1)
+        rep["config"]["staging"] = "one staging pass per owner; the KV-shared layers reuse their source's"
+    if not args.no_cold and not ex["staged"]:
         med = cold_calls(torch, pakv, [lambda l=l: extend_layer(ex, l) for l in range(nl)], pakv.TIME_EXTEND,
                          max(3, args.cold_reps // 4))
         cold = sum(flops) / (sum(med) * 1e-3) / 1e12
-        dom_layers = [l for l, s in enumerate(ex["layers"]) if f"extend_kernel<{s.head_dim}>" == en]
+        dom_layers = [l for l, s in enumerate(ex["layers"]) if f"extend_kernel<{s.head_dim}{tag}>" == en]
         dk = sum(flops[l] for l in dom_layers) / (sum(med[l] for l in dom_layers) * 1e-3) / 1e12
         rep["cold"] = {"value": round(cold, 2), "unit": "TFLOP/s", "frac": round(cold / MFMA_BF16_PEAK_TFLOPS, 4),
                        "dominant_kernel_frac": round(dk / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -642,8 +669,12 @@ def main():
     if not args.no_extend and args.only in (None, "extend"):
         line["extend"] = extend_report(torch, pakv, args)
         progress(f"extend: {line['extend']['value']} TFLOP/s")
+    if not args.no_extend and args.only in (None, "extend_int8"):
+        torch.cuda.empty_cache()
+        line["extend_int8"] = extend_report(torch, pakv, args, kv_dtype="int8")
+        progress(f"int8 extend (staged): {line['extend_int8']['value']} TFLOP/s")
     if "value" not in line:                 # a single non-headline workload (profiling runs)
-        key = next(k for k in ("decode_26b", "decode_int8_long", "extend") if k in line)
+        key = next(k for k in ("decode_26b", "decode_int8_long", "extend", "extend_int8") if k in line)
         line.update(value=line[key]["value"], unit=line[key]["unit"], ms_per_step=line[key]["ms_per_step"],
                     config=line[key]["config"])
     if not args.no_cpu_baseline and st is not None:

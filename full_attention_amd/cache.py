@@ -195,20 +195,33 @@ class PagedKVCache:
         return out
 
     def extend_staged(self, layer, cu_q, prefix_lens, q, max_q_len, max_kv_len, k_ext=None, v_ext=None, out=None,
-                      stream=None):
+                      stream=None, workspace=None, stage=True):
         """Extend on the bf16 MFMA kernel for every format (8-bit slabs, K=V
-        layers and packed chunks staged first into a workspace the cache keeps
-        and grows); k_ext / v_ext as in extend_packed, or None."""
+        layers and packed chunks staged first into a workspace); k_ext / v_ext
+        as in extend_packed, or None.  workspace: a uint8 device tensor of at
+        least staging_bytes(...) bytes, or None for one the cache keeps and
+        grows.  stage=False reuses what an earlier call with the same source
+        layer and arguments staged into that workspace (a KV-shared layer
+        after its source)."""
         nseq = cu_q.shape[0] - 1
         if out is None:
             out = torch.empty_like(q)
-        need = pakv.extend_staging_bytes(self.map, layer, nseq, max_q_len, max_kv_len, k_ext is not None)
-        if need and (self._stage_ws is None or self._stage_ws.numel() < need):
-            self._stage_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
-        ws = self._stage_ws if need else None
+        need = self.staging_bytes(layer, nseq, max_q_len, max_kv_len, k_ext is not None)
+        if workspace is None:
+            if need and (self._stage_ws is None or self._stage_ws.numel() < need):
+                if not stage:
+                    raise ValueError("stage=False needs the workspace an earlier call staged")
+                self._stage_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            workspace = self._stage_ws
+        ws = workspace if need else None
         pakv.paged_attn_extend_staged(self.map, layer, self.pages_of(layer), cu_q, prefix_lens, q, k_ext, v_ext, out,
-                                      nseq, q.shape[0], max_q_len, max_kv_len, ws, need, stream)
+                                      nseq, q.shape[0], max_q_len, max_kv_len, ws,
+                                      workspace.numel() if ws is not None else 0, stage, stream)
         return out
+
+    def staging_bytes(self, layer, num_seqs, max_q_len, max_kv_len, packed=False):
+        """Workspace bytes a staged extend call of this layer needs (0: none)."""
+        return pakv.extend_staging_bytes(self.map, layer, num_seqs, max_q_len, max_kv_len, packed)
 
     def capture_decode_step(self, kv_lens, max_kv_len, layers_io, buckets, max_batch=None):
         """A decode step of the given layers captured into one HIP graph per

@@ -32,6 +32,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "launch_timing.h"
 #include "pakv_internal.h"
 
 using namespace pakv_dev;
@@ -268,8 +269,7 @@ int launch_extend_stage(const ExtendLaunch& s, void* workspace, void* stream) {
                            : (s.kv_dtype == PAKV_KV_INT8_PTH ? kFmtINT8 : (s.kv_dtype == PAKV_KV_FP8_PTH ? kFmtFP8 : kFmtBF16));
     const dim3 grid((unsigned)a.stride, (unsigned)s.hkv, (unsigned)s.num_seqs);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // (not under the timing hook: its events bracket the attention kernel alone)
-#define PAKV_STAGE(DD, FF) hipLaunchKernelGGL((extend_stage_kernel<DD, FF>), grid, dim3(256), 0, st, a)
+#define PAKV_STAGE(DD, FF) launch(PAKV_TIME_STAGE, extend_stage_kernel<DD, FF>, grid, dim3(256), 0, st, a)
     if (s.head_dim == 256) {
         if (f == kFmtINT8) PAKV_STAGE(256, kFmtINT8);
         else if (f == kFmtFP8) PAKV_STAGE(256, kFmtFP8);

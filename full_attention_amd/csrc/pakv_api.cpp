@@ -553,7 +553,8 @@ static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const p
                                const int32_t* cu_q, const int32_t* prefix_lens, const void* q,
                                const void* k_ext, const void* v_ext, void* out,
                                int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
-                               bool packed, void* stream, void* workspace = nullptr, size_t workspace_bytes = 0) {
+                               bool packed, void* stream, void* workspace = nullptr, size_t workspace_bytes = 0,
+                               bool run_stage = true) {
     if (!layer_ok(map, layer)) return fail(PAKV_ERR_INVALID, "bad map or layer %d", layer);
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0) return fail(PAKV_ERR_INVALID, "negative sizes");
     if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PAKV_OK;
@@ -605,7 +606,9 @@ static pakv_status extend_call(const pakv_layer_map* map, int32_t layer, const p
     a.k_eq_v = S.desc.k_eq_v;
     a.v_norm_eps = S.desc.v_norm_eps;
     if (stage) {
-        if (int e = launch_extend_stage(a, workspace, stream)) return hip_status(e, "paged_attn_extend staging launch");
+        if (run_stage)
+            if (int e = launch_extend_stage(a, workspace, stream))
+                return hip_status(e, "paged_attn_extend staging launch");
         // the bf16 kernel on the staged pages: the workspace is its slab
         const int32_t stride = extend_stage_stride(L.desc.window, max_q_len, max_kv_len);
         const int64_t blocks = (int64_t)num_seqs * stride * L.desc.num_kv_heads;
@@ -657,14 +660,14 @@ pakv_status pakv_paged_attn_extend_staged(const pakv_layer_map* map, int32_t lay
                                           const void* q, const void* k_ext, const void* v_ext, void* out,
                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+                                          int32_t stage, void* stream) {
     clear_error();
     const bool packed = k_ext != nullptr;
     if (layer_ok(map, layer) && extend_needs_stage(map, layer, packed) && !workspace && num_seqs > 0 &&
         total_q > 0 && max_q_len > 0)
         return fail(PAKV_ERR_WORKSPACE, "null workspace: layer %d's extend is staged", layer);
     return extend_call(map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q, max_q_len,
-                       max_kv_len, packed, stream, workspace, workspace_bytes);
+                       max_kv_len, packed, stream, workspace, workspace_bytes, stage != 0);
 }
 
 pakv_status pakv_workgroup_xcds(int32_t* out, int32_t num_workgroups, void* stream) {

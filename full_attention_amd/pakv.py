@@ -44,7 +44,7 @@ EXPORTED = (
     "pakv_paged_attn_extend_staged",
 )
 
-TIME_STORE, TIME_DECODE, TIME_EXTEND = 1, 2, 8
+TIME_STORE, TIME_DECODE, TIME_EXTEND, TIME_STAGE = 1, 2, 8, 16
 DECODE_PLAN_MISMATCH, DECODE_XCD_SPLIT = 1, 2     # bits of the decode workspace's status word
 CHECK_XCD_PLACEMENT = 1
 DEBUG_COUNTS = 3                                  # decode plans, stores, extend calls
@@ -122,7 +122,7 @@ lib.pakv_extend_staging_bytes.restype = _S
 lib.pakv_extend_staging_bytes.argtypes = [_P, _I, _I, _I, _I, _I]
 lib.pakv_paged_attn_extend_staged.restype = _I
 lib.pakv_paged_attn_extend_staged.argtypes = [_P, _I, ctypes.POINTER(Pages), _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                              _P, _S, _P]
+                                              _P, _S, _I, _P]
 lib.pakv_page_pool_create.restype = _I
 lib.pakv_page_pool_create.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_P)]
 lib.pakv_page_pool_destroy.restype = None
@@ -324,11 +324,11 @@ def extend_staging_bytes(layer_map, layer, num_seqs, max_q_len, max_kv_len, pack
 
 
 def paged_attn_extend_staged(layer_map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q,
-                             max_q_len, max_kv_len, workspace, workspace_bytes, stream=None):
+                             max_q_len, max_kv_len, workspace, workspace_bytes, stage=True, stream=None):
     return _check(lib.pakv_paged_attn_extend_staged(layer_map.handle, layer, ctypes.byref(pages), _ptr(cu_q),
                                                     _ptr(prefix_lens), _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(out),
                                                     num_seqs, total_q, max_q_len, max_kv_len, _ptr(workspace),
-                                                    workspace_bytes, _stream(stream)))
+                                                    workspace_bytes, 1 if stage else 0, _stream(stream)))
 
 
 def paged_attn_extend_packed(layer_map, layer, pages, cu_q, prefix_lens, q, k_ext, v_ext, out, num_seqs, total_q,

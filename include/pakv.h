@@ -364,8 +364,16 @@ pakv_status pakv_paged_attn_extend_packed(const pakv_layer_map* map, int32_t lay
  *                  pakv_paged_attn_extend_packed
  *   workspace    : device memory of at least pakv_extend_staging_bytes(...,
  *                  packed = k_ext != NULL) bytes (0: none needed; may then be
- *                  NULL); any content; overwritten by the call; calls that
- *                  may overlap need separate workspaces
+ *                  NULL); calls that may overlap need separate workspaces
+ *   stage        : nonzero: the staging pass writes the workspace (any prior
+ *                  content) before the kernel reads it.  0: no staging pass;
+ *                  the workspace holds what an earlier call with stage != 0
+ *                  wrote for a layer with the same source layer (a KV-shared
+ *                  layer and its source stage the same slab), the same
+ *                  pages, cu_q, prefix_lens, k_ext / v_ext contents,
+ *                  num_seqs, max_q_len and max_kv_len, with no store to
+ *                  those positions since; otherwise the results are wrong.
+ *                  Ignored where nothing is staged.
  * Other arguments as in pakv_paged_attn_extend.  Errors: PAKV_ERR_WORKSPACE for
  * a missing or short workspace, else as pakv_paged_attn_extend. */
 size_t pakv_extend_staging_bytes(const pakv_layer_map* map, int32_t layer, int32_t num_seqs, int32_t max_q_len,
@@ -375,7 +383,7 @@ pakv_status pakv_paged_attn_extend_staged(const pakv_layer_map* map, int32_t lay
                                           const void* q, const void* k_ext, const void* v_ext, void* out,
                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, void* workspace, size_t workspace_bytes,
-                                          void* stream);
+                                          int32_t stage, void* stream);
 
 /* ---- Decode step graphs ---------------------------------------------------------
  * A whole decode step of a layer stack, captured once per batch-size bucket
@@ -520,6 +528,7 @@ pakv_status pakv_debug_bounds_reset(void);
 #define PAKV_TIME_STORE 1           /* the store kernel */
 #define PAKV_TIME_DECODE 2          /* the decode kernel */
 #define PAKV_TIME_EXTEND 8          /* the extend kernel */
+#define PAKV_TIME_STAGE 16          /* the staging pass of pakv_paged_attn_extend_staged */
 pakv_status pakv_set_timing_events(void* const* events, int32_t n_pairs, int32_t kernel_mask);
 /* Number of event pairs recorded on this thread since the hook was last set. */
 int32_t pakv_timing_pairs_used(void);

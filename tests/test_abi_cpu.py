@@ -202,16 +202,16 @@ def test_extend_staging_sizes_and_refusals():
     lib = pakv.lib
     need = pakv.extend_staging_bytes(m, 2, 2, 5, 40, False)
     assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, None, None,
-                                             0x7000, 2, 10, 5, 40, None, 0, None) == pakv.ERR_WORKSPACE
+                                             0x7000, 2, 10, 5, 40, None, 0, 1, None) == pakv.ERR_WORKSPACE
     assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, None, None,
-                                             0x7000, 2, 10, 5, 40, 0x9000, need - 1, None) == pakv.ERR_WORKSPACE
+                                             0x7000, 2, 10, 5, 40, 0x9000, need - 1, 1, None) == pakv.ERR_WORKSPACE
     assert "staging" in pakv.last_error()
     # packed on a bf16 layer needs staging too; without its value rows it is refused
     assert lib.pakv_paged_attn_extend_staged(m.handle, 0, ctypes.byref(pages), 0x6000, 0x6100, 0x6200, 0x6300, None,
-                                             0x7000, 2, 10, 5, 40, 0x9000, 1 << 30, None) == pakv.ERR_INVALID
+                                             0x7000, 2, 10, 5, 40, 0x9000, 1 << 30, 1, None) == pakv.ERR_INVALID
     # empty chunk: nothing to do, no workspace needed
     assert lib.pakv_paged_attn_extend_staged(m.handle, 2, ctypes.byref(pages), None, None, None, None, None,
-                                             None, 2, 0, 0, 40, None, 0, None) == pakv.OK
+                                             None, 2, 0, 0, 40, None, 0, 1, None) == pakv.OK
 
 
 def test_unbound_source_slab_is_an_error():

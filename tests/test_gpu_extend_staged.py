@@ -175,3 +175,29 @@ def test_staged_agrees_with_the_unstaged_kernel_and_repeats_exactly(fmt, d, wind
     a = bf16_to_f32(runs[0]).astype(np.float64)
     g = bf16_to_f32(general).astype(np.float64)
     assert (np.abs(a - g) <= 2e-2 + 1e-2 * np.abs(g)).all(), np.abs(a - g).max()
+
+
+@pytest.mark.parametrize("fmt,d,window", [("int8", 256, 32), ("keqv", 512, 0), ("fp8", 512, 0)])
+def test_shared_layer_reuses_its_source_staging(fmt, d, window):
+    """A KV-shared layer called with stage=False on the workspace its source's
+    call staged: bit-identical to its own staging pass, and matches the
+    oracle."""
+    need_gpu()
+    caps = [p + n for p, n in zip(LONG_PREFIXES, LONG_CHUNKS)]
+    specs = [_spec(fmt, d, 8, 1, window), _spec(fmt, d, 8, 1, window)]
+    sc = Scenario(specs, 1, caps, seed=zlib.crc32(repr(("reuse", fmt, d)).encode()) % 1000)
+    sc.store(0, [0] * len(caps), caps)
+    total = sum(LONG_CHUNKS)
+    cu = np.concatenate([[0], np.cumsum(LONG_CHUNKS)]).astype(np.int32)
+    max_q, max_kv = max(LONG_CHUNKS), max(p + n for p, n in zip(LONG_PREFIXES, LONG_CHUNKS))
+    need = sc.cache.staging_bytes(0, len(caps), max_q, max_kv)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    args = (i32(cu), i32(LONG_PREFIXES))
+    q0 = normal_bf16(sc.rng, (total, 8, d))
+    q1 = normal_bf16(sc.rng, (total, 8, d))
+    sc.cache.extend_staged(0, *args, dev_bits(q0), max_q, max_kv, workspace=ws, stage=True)
+    reused = host_bits(sc.cache.extend_staged(1, *args, dev_bits(q1), max_q, max_kv, workspace=ws, stage=False))
+    fresh = host_bits(sc.cache.extend_staged(1, *args, dev_bits(q1), max_q, max_kv))
+    torch.cuda.synchronize()
+    assert np.array_equal(reused, fresh)
+    _check(sc, 1, LONG_PREFIXES, LONG_CHUNKS, reused, q1, cu, f"reused staging {fmt} d={d} W={window}")
