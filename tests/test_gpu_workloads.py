@@ -195,6 +195,44 @@ def test_e2b_extend_full_size():
             assert_close(out[cu[b] + rows], ref, f"E2B extend layer {l} seq {b}", report=(l in (0, 4)))
 
 
+def test_e2b_extend_int8_staged_full_size():
+    """The extend stack with int8 per-token-head KV on every layer, in the
+    launch configuration bench.py times for it: the staged call, one staging
+    pass per owner, the KV-shared layers reusing their source's workspace.
+    Sampled rows of every sequence against the oracle (on the oracle's own
+    int8 encoding of the drawn rows); row 0 of the empty-prefix sequence sees
+    one key, so its output is that key's value row."""
+    import dataclasses
+    need_gpu()
+    wl = e2b_extend_workload()
+    wl = dataclasses.replace(wl, layers=[dataclasses.replace(s, kv_dtype="int8") for s in wl.layers])
+    P = np.array(wl.cached_lens, dtype=np.int64)
+    n = np.array(wl.extend_lens, dtype=np.int64)
+    sc = DeviceScenario(wl, P + n, range(len(P)))
+    for l, s in enumerate(wl.layers):
+        lo = np.maximum(0, P - s.window + 1) if s.window else np.zeros_like(P)
+        sc.store(l, lo, P - lo)
+    cu = np.concatenate([[0], np.cumsum(n)])
+    max_q, max_kv = int(n.max()), int((P + n).max())
+    ws = {}
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 511, 512, 513, 1023, 2047], rng.integers(0, 2048, 7)]))
+    for l, s in enumerate(wl.layers):
+        sc.store(l, P, n)
+        src = sc.cache.sources[l]
+        if src == l:
+            ws[l] = torch.empty(sc.cache.staging_bytes(l, len(P), max_q, max_kv), dtype=torch.uint8, device="cuda")
+        q = sc.draws.bf16((int(cu[-1]), s.num_q_heads, s.head_dim))
+        out = host_bits(sc.cache.extend_staged(l, i32(cu), i32(P), q, max_q, max_kv, workspace=ws[src],
+                                               stage=src == l))
+        qf = f64(q)
+        for b in range(len(P)):
+            pos, k, v = sc.rows(l, b)
+            ref = attend(qf[cu[b] + rows], P[b] + rows, k, v, pos, s.window, s.sm_scale)
+            assert_close(out[cu[b] + rows], ref, f"E2B int8 staged extend layer {l} seq {b}",
+                         report=(l in (0, 4, 20)))
+
+
 # ---- closed forms at full size ------------------------------------------------
 # With q = 0 every visible key scores 0, so the output is the plain mean of the
 # visible value rows, whatever the keys hold.  Value row j carries A = D in one
