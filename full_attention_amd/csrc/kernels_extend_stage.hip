@@ -111,9 +111,11 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
     const bool any_slab = 16 * pg < first_ext;
     const int64_t blk = any_slab ? slab_blk() : 0;
 
-    // ---- keys: thread = (token tt, dims seg .. seg + SEG) ---------------------
+    // ---- keys: thread = (token tt, 8 dims at seg + 128 c for c < SEG / 8), so
+    // that the 16 threads of a row read and write 128 / 256 contiguous bytes
+    // per instruction ---------------------------------------------------------
     {
-        const int tt = tid >> 4, seg = (tid & 15) * SEG;
+        const int tt = tid >> 4, seg = (tid & 15) * 8;
         const int32_t pos = 16 * pg + tt;
         const bool live = pos >= lo && pos < hi;
         const bool ext = pos >= first_ext;
@@ -123,14 +125,14 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
         for (int c = 0; c < SEG / 8; ++c) {
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (live && ext) {
-                x = *reinterpret_cast<const u32x4*>(a.k_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 8 * c);
+                x = *reinterpret_cast<const u32x4*>(a.k_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 128 * c);
             } else if (live) {
-                const uint8_t* src = a.k_slab + ((blk * 16 + tt) * D + seg + 8 * c) * ES;
+                const uint8_t* src = a.k_slab + ((blk * 16 + tt) * D + seg + 128 * c) * ES;
                 if constexpr (Q8) x = codes8_to_bf16x8<F>(*reinterpret_cast<const u32x2*>(src));
                 else x = *reinterpret_cast<const u32x4*>(src);
             }
-            *reinterpret_cast<u32x4*>(dst + 8 * c) = x;
-            *reinterpret_cast<u32x4*>(kt + tt * D + seg + 8 * c) = x;
+            *reinterpret_cast<u32x4*>(dst + 128 * c) = x;
+            *reinterpret_cast<u32x4*>(kt + tt * D + seg + 128 * c) = x;
             if constexpr (F == kFmtKEQV) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) ss = sq_sum_bf16x2(x[w], ss);
@@ -159,15 +161,15 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
     }
     // packed value rows of the page, token-major, for the transpose below
     if (F != kFmtKEQV && packed && 16 * pg + 15 >= first_ext) {
-        const int tt = tid >> 4, seg = (tid & 15) * SEG;
+        const int tt = tid >> 4, seg = (tid & 15) * 8;
         const int32_t pos = 16 * pg + tt;
         const bool take = pos >= first_ext && pos >= lo && pos < hi;
 #pragma unroll
         for (int c = 0; c < SEG / 8; ++c) {
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (take)
-                x = *reinterpret_cast<const u32x4*>(a.v_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 8 * c);
-            *reinterpret_cast<u32x4*>(vt + tt * D + seg + 8 * c) = x;
+                x = *reinterpret_cast<const u32x4*>(a.v_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 128 * c);
+            *reinterpret_cast<u32x4*>(vt + tt * D + seg + 128 * c) = x;
         }
     }
     __syncthreads();
