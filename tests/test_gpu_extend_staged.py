@@ -201,3 +201,60 @@ def test_shared_layer_reuses_its_source_staging(fmt, d, window):
     torch.cuda.synchronize()
     assert np.array_equal(reused, fresh)
     _check(sc, 1, LONG_PREFIXES, LONG_CHUNKS, reused, q1, cu, f"reused staging {fmt} d={d} W={window}")
+
+
+def _random_case(seed):
+    """A seeded random staged-extend case: format, head dim, GQA shape,
+    window, batch, prefixes and chunk lengths (an empty chunk possible),
+    packed or not."""
+    r = np.random.default_rng(seed)
+    fmt = ["int8", "fp8", "keqv", "bf16"][r.integers(0, 4)]
+    packed = fmt == "bf16" or bool(r.integers(0, 2))
+    d = int(r.choice([256, 512]))
+    hkv = int(r.choice([1, 2, 4]))
+    hq = hkv * int(r.choice([1, 2, 3, 8]))
+    window = int(r.choice([0, 0, 1, 2, 17, 32, 33, 100, 512]))
+    B = int(r.integers(1, 6))
+    prefixes = [int(x) for x in r.integers(0, 300, B)]
+    chunks = [int(x) for x in r.integers(0, 120, B)]
+    if r.integers(0, 3) == 0:
+        chunks[int(r.integers(0, B))] = 0
+    if sum(chunks) == 0:
+        chunks[0] = 1
+    return fmt, packed, d, hq, hkv, window, prefixes, chunks
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_staged_random_shapes_match_oracle(seed):
+    need_gpu()
+    fmt, packed, d, hq, hkv, window, prefixes, chunks = _random_case(9000 + seed)
+    what = f"seed {seed}: {fmt} packed={packed} d={d} hq={hq} hkv={hkv} W={window} P={prefixes} n={chunks}"
+    print(what, flush=True)
+    caps = [max(p + n, 1) for p, n in zip(prefixes, chunks)]
+    sc = Scenario([_spec(fmt, d, hq, hkv, window)], None, caps, seed=seed)
+    kve = fmt == "keqv"
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    total = int(cu[-1])
+    max_q, max_kv = max(chunks), max(p + n for p, n in zip(prefixes, chunks))
+    q = normal_bf16(sc.rng, (total, hq, d))
+    if packed:
+        sc.store(0, [0] * len(caps), prefixes)
+        k = normal_bf16(sc.rng, (total, hkv, d))
+        v = normal_bf16(sc.rng, (total, hkv, d))
+        _poison_workspace(sc, 0, len(chunks), max_q, max_kv, True)
+        got = host_bits(sc.cache.extend_staged(0, i32(cu), i32(prefixes), dev_bits(q), max_q, max_kv,
+                                               k_ext=dev_bits(k), v_ext=None if kve else dev_bits(v)))
+    else:
+        sc.store(0, [0] * len(caps), [p + n for p, n in zip(prefixes, chunks)])
+        _poison_workspace(sc, 0, len(chunks), max_q, max_kv, False)
+        got = host_bits(sc.cache.extend_staged(0, i32(cu), i32(prefixes), dev_bits(q), max_q, max_kv))
+    torch.cuda.synchronize()
+    for b, n in enumerate(chunks):
+        if n == 0:
+            continue
+        if packed:
+            ref = sc.oracle.extend_packed(0, b, q[cu[b]:cu[b + 1]], prefixes[b], k[cu[b]:cu[b + 1]],
+                                          None if kve else v[cu[b]:cu[b + 1]])
+        else:
+            ref = sc.oracle.extend(0, b, q[cu[b]:cu[b + 1]], prefixes[b])
+        assert_close(got[cu[b]:cu[b + 1]], ref, f"{what} seq {b}")
