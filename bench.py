@@ -63,14 +63,14 @@ def parse():
     ap.add_argument("--extend-steps", type=int, default=3)
     ap.add_argument("--cold-reps", type=int, default=20, help="timed repetitions per call of the cold figures")
     ap.add_argument("--no-extend", action="store_true")
-    ap.add_argument("--no-other-decode", action="store_true", help="skip the 26B-like and int8 long-context steps")
+    ap.add_argument("--no-other-decode", action="store_true", help="skip the 26B-like and the int8 and fp8 long-context steps")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
     ap.add_argument("--eager", action="store_true", help="launch the decode steps eagerly instead of from graphs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["e2b", "26b", "int8", "extend", "extend_int8"], default=None,
+    ap.add_argument("--only", choices=["e2b", "26b", "int8", "fp8", "extend", "extend_int8"], default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--no-ladder", action="store_true",
                     help="skip the per-batch-bucket step times (profiling runs: every dispatch is then one of "
@@ -117,6 +117,7 @@ EXTEND_WL = "E2B-like extend, 35 layers, 4 sequences"
 E2B_WL = "E2B-like decode, 35 layers, batch 64"
 MOE_WL = "26B-like decode, 30 layers, batch 48"
 INT8_WL = "int8 long decode, batch 8 x 131072"
+FP8_WL = "fp8 long decode, batch 8 x 131072"
 
 
 class Timing:
@@ -666,6 +667,20 @@ def main():
         progress(f"int8 long decode: {line['decode_int8_long']['value']} GB/s")
         del lo
         torch.cuda.empty_cache()
+    if not args.no_other_decode and args.only in (None, "fp8"):
+        import dataclasses
+        wl8 = int8_long_workload()
+        wl8 = dataclasses.replace(wl8, layers=[dataclasses.replace(s, kv_dtype="fp8") for s in wl8.layers])
+        f8 = setup_decode(torch, wl8, window_pool=True)
+        progress("fp8 long decode set up")
+        line["decode_fp8_long"] = decode_report(torch, pakv, f8, args, FP8_WL, {
+            "workload": FP8_WL + " (the int8 long-context workload with fp8 E4M3 per-token-head KV: one full "
+                                 "D512 and one sliding D256 W1024 layer, Hq 8 Hkv 1; " + f8["pool_note"] + ")",
+            "global_batch": f8["B"], "seq_len": int(f8["max_kv_len"]), "layers": 2,
+            "step": "plan 2 kinds of layer + 2 fp8 owners store their new row then decode"})
+        progress(f"fp8 long decode: {line['decode_fp8_long']['value']} GB/s")
+        del f8
+        torch.cuda.empty_cache()
     if not args.no_extend and args.only in (None, "extend"):
         line["extend"] = extend_report(torch, pakv, args)
         progress(f"extend: {line['extend']['value']} TFLOP/s")
@@ -674,7 +689,8 @@ def main():
         line["extend_int8"] = extend_report(torch, pakv, args, kv_dtype="int8")
         progress(f"int8 extend (staged): {line['extend_int8']['value']} TFLOP/s")
     if "value" not in line:                 # a single non-headline workload (profiling runs)
-        key = next(k for k in ("decode_26b", "decode_int8_long", "extend", "extend_int8") if k in line)
+        key = next(k for k in ("decode_26b", "decode_int8_long", "decode_fp8_long", "extend", "extend_int8")
+                   if k in line)
         line.update(value=line[key]["value"], unit=line[key]["unit"], ms_per_step=line[key]["ms_per_step"],
                     config=line[key]["config"])
     if not args.no_cpu_baseline and st is not None:

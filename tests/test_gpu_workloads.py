@@ -1,5 +1,6 @@
-"""The five workloads at full size, run the way bench.py runs them (same
-kernels, same grid), checked against the oracle on sampled outputs.
+"""The five workloads at full size (and the long-context one with fp8 KV),
+run the way bench.py runs them (same kernels, same grid), checked against the
+oracle on sampled outputs.
 
 Rows are drawn on the device by a seeded generator (workloads.DeviceDraws),
 stored through paged_kv_store, and the rows of the sampled sequences are
@@ -11,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, quantise_rows, dequantise_rows, v_from_k
+from oracle import attend, fp8_pth, quantise_rows, dequantise_rows, v_from_k
 from workloads.configs import V_NORM_EPS
 from workloads import (DeviceDraws, bf16_to_f32, e2b_decode_workload, e2b_extend_workload,
                        int8_long_workload, make_page_pool, moe26b_decode_workload, tiny_workload)
@@ -80,6 +81,10 @@ class DeviceScenario:
             kq, ks = quantise_rows(k)
             vq, vs = quantise_rows(v)
             k, v = dequantise_rows(kq, ks), dequantise_rows(vq, vs)
+        elif spec.kv_dtype == "fp8":
+            kq, ks = fp8_pth.quantise_rows(k)
+            vq, vs = fp8_pth.quantise_rows(v)
+            k, v = fp8_pth.dequantise_rows(kq, ks), fp8_pth.dequantise_rows(vq, vs)
         if spec.k_eq_v and self.cache.specs[layer]["k_eq_v"]:
             # one slab: the library derives the values from the stored keys
             return pos, k.astype(np.float64), v_from_k(k, V_NORM_EPS)
@@ -170,6 +175,18 @@ def test_moe26b_decode_full_size():
 def test_int8_long_context_full_size():
     need_gpu()
     _decode_workload(int8_long_workload(), n_sample=2)
+
+
+def test_fp8_long_context_full_size():
+    """The long-context workload with fp8 E4M3 per-token-head KV, as
+    bench.py's decode_fp8_long runs it (the oracle on its own E4M3 encoding
+    of the drawn rows)."""
+    import dataclasses
+    need_gpu()
+    wl = int8_long_workload()
+    wl = dataclasses.replace(wl, name=wl.name + " (fp8)",
+                             layers=[dataclasses.replace(s, kv_dtype="fp8") for s in wl.layers])
+    _decode_workload(wl, n_sample=2)
 
 
 def test_e2b_extend_full_size():
@@ -281,8 +298,8 @@ def _check_bucket_decode(wl, sample, seqs_label):
             ref = attend(np.zeros((1, s.num_q_heads, s.head_dim)), np.array([kv[b] - 1]), k, v, pos, s.window,
                          s.sm_scale)[0]
             closed = _closed_form_mean(s.window, int(kv[b]), s.head_dim, n_vis[l])
-            # the oracle agrees with the closed form (int8: to the encoding's error)
-            tol = 1e-3 if s.kv_dtype == "int8" else 1e-9
+            # the oracle agrees with the closed form (8-bit: to the encoding's error)
+            tol = 1e-3 if s.kv_dtype in ("int8", "fp8") else 1e-9
             assert np.abs(ref - closed[None, :]).max() < tol
             assert_close(got[b], ref, f"{wl.name} {seqs_label} layer {l} seq {b}: q = 0, one-hot values", report=True)
 
@@ -291,6 +308,16 @@ def test_int8_long_context_every_page_counts():
     """131,073 keys per sequence, all 8 sequences, both int8 layers."""
     need_gpu()
     _check_bucket_decode(int8_long_workload(), list(range(8)), "all sequences")
+
+
+def test_fp8_long_context_every_page_counts():
+    """The same with fp8 E4M3 per-token-head KV (bench.py's decode_fp8_long)."""
+    import dataclasses
+    need_gpu()
+    wl = int8_long_workload()
+    wl = dataclasses.replace(wl, name=wl.name + " (fp8)",
+                             layers=[dataclasses.replace(s, kv_dtype="fp8") for s in wl.layers])
+    _check_bucket_decode(wl, list(range(8)), "all sequences")
 
 
 def test_moe26b_longest_sequence_every_page_counts():
