@@ -419,11 +419,10 @@ __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, 
             const int h8 = (lane_id_here() >> 5) << 3;
             const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 16 + h8);
             const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 16 + h8 + 4);
-            // (a weight of 0 stays 0: a key outside the staged range may
-            // carry any scale)
-            auto w = [](float p, float v) { return p != 0.f ? p * v : 0.f; };
-            pb0 = u32x4{cvt_pk_bf16(w(s[0], v0[0]), w(s[1], v0[1])), cvt_pk_bf16(w(s[2], v0[2]), w(s[3], v0[3])),
-                        cvt_pk_bf16(w(s[4], v1[0]), w(s[5], v1[1])), cvt_pk_bf16(w(s[6], v1[2]), w(s[7], v1[3]))};
+            // (every staged scale is finite, zero outside the staged range,
+            // so a masked key's weight 0 stays 0)
+            pb0 = u32x4{cvt_pk_bf16(s[0] * v0[0], s[1] * v0[1]), cvt_pk_bf16(s[2] * v0[2], s[3] * v0[3]),
+                        cvt_pk_bf16(s[4] * v1[0], s[5] * v1[1]), cvt_pk_bf16(s[6] * v1[2], s[7] * v1[3])};
         } else {
             pb0 = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]), cvt_pk_bf16(s[4], s[5]),
                         cvt_pk_bf16(s[6], s[7])};
@@ -437,9 +436,8 @@ __device__ __forceinline__ void softmax_pack_hi(const f32x16& s, u32x4& pb1, con
         const int h8 = (lane_id_here() >> 5) << 3;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 48 + h8);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 48 + h8 + 4);
-        auto w = [](float p, float v) { return p != 0.f ? p * v : 0.f; };
-        pb1 = u32x4{cvt_pk_bf16(w(s[8], v0[0]), w(s[9], v0[1])), cvt_pk_bf16(w(s[10], v0[2]), w(s[11], v0[3])),
-                    cvt_pk_bf16(w(s[12], v1[0]), w(s[13], v1[1])), cvt_pk_bf16(w(s[14], v1[2]), w(s[15], v1[3]))};
+        pb1 = u32x4{cvt_pk_bf16(s[8] * v0[0], s[9] * v0[1]), cvt_pk_bf16(s[10] * v0[2], s[11] * v0[3]),
+                    cvt_pk_bf16(s[12] * v1[0], s[13] * v1[1]), cvt_pk_bf16(s[14] * v1[2], s[15] * v1[3])};
     } else {
         pb1 = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]), cvt_pk_bf16(s[12], s[13]),
                     cvt_pk_bf16(s[14], s[15])};

@@ -20,7 +20,8 @@
 //     values are the unscaled RMS-normalised keys);
 //   - positions outside the range any row of the chunk sees are staged as
 //     zeros with zero scales, so a never-written slot (possibly NaN) never
-//     reaches the arithmetic.
+//     reaches the arithmetic; pages past the last row's end get zero scales
+//     only (their K and V are masked and zeroed by the kernel).
 // Layout: sequence b's staged pages are workspace pages b * stride + j, page
 // j holding positions 16 (2 (lo_b / 32) + j) .. + 15, where lo_b is the first
 // position its first row sees (0 on a full layer): whole 32-key tiles of the
@@ -87,15 +88,21 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
     const int32_t j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int32_t q0 = a.cu_q[b];
     const int32_t n = min(a.cu_q[b + 1] - q0, a.max_q_len);
-    if (n <= 0) return;                          // no row of b reads anything
     const int32_t P = a.prefix_lens[b];
     const int32_t hi = min(P + n, a.max_kv_len);                          // the last row's end
     const int32_t lo = (a.window > 0) ? max(0, P - a.window + 1) : 0;     // the first row's start
     const int32_t pg = 2 * (lo / 32) + j;
-    if (16 * pg >= hi) return;                   // past every row's range: never read
-    const bool packed = a.k_ext != nullptr;
     const int64_t sblk = ((int64_t)b * a.stride + j) * a.hkv + g;
     float* ssc = a.ssc + ((int64_t)g * gridDim.z * a.stride + (int64_t)b * a.stride + j) * 32;
+    // a page no row reads (past the last row's end, or of a sequence with no
+    // rows): its K and V are never staged, but its scales are zeros, so that
+    // every scale the kernel can meet is finite (a masked key's weight, 0,
+    // times its value scale is then 0)
+    if (n <= 0 || 16 * pg >= hi) {
+        if (tid < 32) ssc[tid] = 0.f;
+        return;
+    }
+    const bool packed = a.k_ext != nullptr;
 
     // the slab block of this page (read only for live tokens below the chunk
     // when packed); an id outside the pool reads page 0, as the kernels do
