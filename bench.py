@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--extend-steps", type=int, default=3)
     ap.add_argument("--cold-reps", type=int, default=20, help="timed repetitions per call of the cold figures")
     ap.add_argument("--no-extend", action="store_true")
-    ap.add_argument("--no-other-decode", action="store_true", help="skip the 26B-like and the int8 and fp8 long-context steps")
+    ap.add_argument("--no-other-decode", action="store_true",
+                    help="skip the 26B-like and the int8 and fp8 long-context steps")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")

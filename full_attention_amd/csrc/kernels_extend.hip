@@ -350,9 +350,10 @@ struct SoftRow {
 // inv_g = 1 / G: (x + 1/2) / G lies at least 1/(2G) from an integer, far
 // beyond the float product's error, so the floor is exact.
 // SC (the staged kernel): sc holds the tile's scales, per page the 16 key
-// scales then the 16 value scales of its tokens; stage 0 multiplies each score by its key's scale
-// before anything else, and the packing multiplies each weight by its key's
-// value scale (the row sum takes the weights as they are).
+// scales then the 16 value scales of its tokens; stage 0 multiplies each
+// score by its key's scale before anything else, and the packing multiplies
+// each weight by its key's value scale (the row sum takes the weights as
+// they are).
 template <bool FRESH, bool SC>
 __device__ __forceinline__ void softmax_stage(int stage, f32x16& s, SoftRow& r, int32_t t0, bool whole,
                                               int32_t row_lo, int32_t row_hi, int32_t window, int h,

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
         for (int c = 0; c < SEG / 8; ++c) {
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (live && ext) {
-                x = *reinterpret_cast<const u32x4*>(a.k_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 128 * c);
+                x = *reinterpret_cast<const u32x4*>(a.k_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg +
+                                                     128 * c);
             } else if (live) {
                 const uint8_t* src = a.k_slab + ((blk * 16 + tt) * D + seg + 128 * c) * ES;
                 if constexpr (Q8) x = codes8_to_bf16x8<F>(*reinterpret_cast<const u32x2*>(src));
@@ -175,7 +176,8 @@ __global__ __launch_bounds__(256) void extend_stage_kernel(StageArgs a) {
         for (int c = 0; c < SEG / 8; ++c) {
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (take)
-                x = *reinterpret_cast<const u32x4*>(a.v_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg + 128 * c);
+                x = *reinterpret_cast<const u32x4*>(a.v_ext + ((int64_t)(q0 + pos - P) * a.hkv + g) * D + seg +
+                                                     128 * c);
             *reinterpret_cast<u32x4*>(vt + tt * D + seg + 128 * c) = x;
         }
     }
@@ -274,8 +276,10 @@ int launch_extend_stage(const ExtendLaunch& s, void* workspace, void* stream) {
     w += al(blocks * 16 * s.head_dim * 2);
     a.ssc = reinterpret_cast<float*>(w);
     a.bad_ids = debug_bad_ids_ptr();
-    const int f = s.k_eq_v ? kFmtKEQV
-                           : (s.kv_dtype == PAKV_KV_INT8_PTH ? kFmtINT8 : (s.kv_dtype == PAKV_KV_FP8_PTH ? kFmtFP8 : kFmtBF16));
+    const int f = s.k_eq_v                         ? kFmtKEQV
+                  : s.kv_dtype == PAKV_KV_INT8_PTH ? kFmtINT8
+                  : s.kv_dtype == PAKV_KV_FP8_PTH  ? kFmtFP8
+                                                   : kFmtBF16;
     const dim3 grid((unsigned)a.stride, (unsigned)s.hkv, (unsigned)s.num_seqs);
     hipStream_t st = static_cast<hipStream_t>(stream);
 #define PAKV_STAGE(DD, FF) launch(PAKV_TIME_STAGE, extend_stage_kernel<DD, FF>, grid, dim3(256), 0, st, a)
