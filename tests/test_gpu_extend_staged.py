@@ -258,3 +258,44 @@ def test_staged_random_shapes_match_oracle(seed):
         else:
             ref = sc.oracle.extend(0, b, q[cu[b]:cu[b + 1]], prefixes[b])
         assert_close(got[cu[b]:cu[b + 1]], ref, f"{what} seq {b}")
+
+
+@pytest.mark.parametrize("fmt,packed", [("int8", False), ("keqv", True)])
+def test_staged_extend_in_graph_replays(fmt, packed):
+    """The staged call (staging pass + scaled kernel) captured into a HIP graph:
+    every replay, with unrelated eager work between replays, gives the eager
+    call's bits (the call launches no memset and allocates nothing)."""
+    need_gpu()
+    caps = [p + n for p, n in zip(LONG_PREFIXES, LONG_CHUNKS)]
+    sc = Scenario([_spec(fmt, 512, 8, 1, 0)], None, caps, seed=303 if packed else 302)
+    sc.store(0, [0] * len(caps), LONG_PREFIXES if packed else caps)
+    total = sum(LONG_CHUNKS)
+    cu = i32(np.concatenate([[0], np.cumsum(LONG_CHUNKS)]))
+    pre = i32(LONG_PREFIXES)
+    max_q, max_kv = max(LONG_CHUNKS), max(p + n for p, n in zip(LONG_PREFIXES, LONG_CHUNKS))
+    q = dev_bits(normal_bf16(sc.rng, (total, 8, 512)))
+    kx = dev_bits(normal_bf16(sc.rng, (total, 1, 512))) if packed else None
+    ws = torch.empty(sc.cache.staging_bytes(0, len(caps), max_q, max_kv, packed), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def call():
+        sc.cache.extend_staged(0, cu, pre, q, max_q, max_kv, k_ext=kx, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(0)
+        ws.fill_(0xFF)                                   # the replay must restage
+        torch.randn(1000, device="cuda").sum()          # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
