@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import LayerSpec, bf16_to_f32, normal_bf16
+from workloads import LayerSpec, bf16_from_f32, bf16_to_f32, normal_bf16
 
 from gpu_helpers import Scenario, assert_close, dev_bits, host_bits, i32, need_gpu
 
@@ -591,3 +591,25 @@ def test_stream_k_runs_cross_units_and_xcd_blocks():
     assert np.any((w0 != w1) & (w0 // 64 == w1 // 64)) and np.any(w0 // 64 != w1 // 64)
     ref = np.stack([sc.oracle.decode(0, b, q[b], L) for b, L in enumerate(lens)])
     assert_close(out, ref)
+
+
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("q_scale", [2.0 ** -20, 2.0 ** 6])
+def test_int8_decode_with_tiny_and_large_queries(d, q_scale):
+    """int8 scores run on fp16 MFMAs with Q scaled per wavefront by a power of
+    two: queries 2^20 times smaller (near-uniform weights) or 2^6 times larger
+    (peaked weights) than N(0, 1) still match the oracle; heads of one unit
+    differ in magnitude by 2^10."""
+    need_gpu()
+    spec = LayerSpec("full", d, 8, 1, 0, kv_dtype="int8")
+    lens = [1, 33, 700, 2049]
+    sc = Scenario([spec], None, lens, seed=417 if q_scale < 1 else 418)
+    sc.store(0, [0] * len(lens), lens)
+    q = normal_bf16(sc.rng, (len(lens), 8, d))
+    qf = bf16_to_f32(q) * np.float32(q_scale)
+    qf[:, :4] *= np.float32(2.0 ** 10) if q_scale < 1 else np.float32(2.0 ** -10)
+    q = bf16_from_f32(qf)                       # power-of-two scaling: the same bf16 mantissas
+    out = host_bits(sc.cache.decode(0, i32(lens), dev_bits(q), max(lens)))
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        assert_close(out[b], sc.oracle.decode(0, b, q[b], L), f"int8 d={d} q x {q_scale} seq {b}")
