@@ -852,7 +852,7 @@ __device__ __forceinline__ void q_to_f16(u32x4 (&qreg)[N], float& q_inv, float& 
     for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
     am = wave_max_across_groups(am);
     const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(am));
-    const int sh = min(60, max(-60, 15 - e));
+    const int sh = min(126, max(-126, 15 - e));     // 2^sh and 2^-sh stay normal floats
     const float sc = __builtin_amdgcn_ldexpf(1.0f, sh);
     q_inv = __builtin_amdgcn_ldexpf(1.0f, -sh);
     float sum = 0.f;

@@ -594,12 +594,13 @@ def test_stream_k_runs_cross_units_and_xcd_blocks():
 
 
 @pytest.mark.parametrize("d", [256, 512])
-@pytest.mark.parametrize("q_scale", [2.0 ** -20, 2.0 ** 6])
+@pytest.mark.parametrize("q_scale", [2.0 ** -20, 2.0 ** 6, 2.0 ** 80])
 def test_int8_decode_with_tiny_and_large_queries(d, q_scale):
     """int8 scores run on fp16 MFMAs with Q scaled per wavefront by a power of
-    two: queries 2^20 times smaller (near-uniform weights) or 2^6 times larger
-    (peaked weights) than N(0, 1) still match the oracle; heads of one unit
-    differ in magnitude by 2^10."""
+    two: queries 2^20 times smaller (near-uniform weights), 2^6 times larger
+    (peaked weights) or 2^80 times larger (far past fp16's range: one-hot
+    weights) than N(0, 1) still match the oracle; heads of one unit differ in
+    magnitude by 2^10."""
     need_gpu()
     spec = LayerSpec("full", d, 8, 1, 0, kv_dtype="int8")
     lens = [1, 33, 700, 2049]
