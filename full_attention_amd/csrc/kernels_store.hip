@@ -300,6 +300,122 @@ __global__ __launch_bounds__(256) void store_q8_kernel(StoreArgs a) {
     }
 }
 
+// Chunk stores of 8-bit rows: one workgroup per 16 consecutive tokens of the
+// flat list and KV head, as store_bf16_pages_kernel.  Wavefront w encodes rows
+// 4w .. 4w + 3 exactly as the row kernel does (same amax, scale and codes);
+// the K codes go straight to their rows, the V codes to LDS, and when the 16
+// tokens fill one page each dim's 16 codes leave as one 16-byte dim-major row
+// (the row kernel writes D single bytes per token).
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void store_q8_pages_kernel(StoreArgs a) {
+    constexpr int EPL = D / 64;
+    constexpr float kMax = FP8 ? 448.0f : 127.0f;
+    __shared__ int64_t head_of[16];            // phys page * hkv + h, or -1
+    __shared__ int32_t slot_of[16];
+    __shared__ __attribute__((aligned(16))) uint8_t vq[16 * D];   // V codes, token-major
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int32_t t0 = blockIdx.x * 16;
+    const int32_t h = blockIdx.y;
+    const int32_t nt = min(16, a.total_tokens - t0);
+    // the rows of this wavefront, fetched before their places are known
+    float kx[4][EPL], vx[4][EPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = 4 * wave + r;
+        const int64_t src = ((int64_t)(t0 + j) * a.hkv + h) * D + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            kx[r][e] = j < nt ? bf16_bits_to_f32(a.k[src + e]) : 0.0f;
+            vx[r][e] = j < nt ? bf16_bits_to_f32(a.v[src + e]) : 0.0f;
+        }
+    }
+    if (t < 64) {
+        const int32_t b = find_seq(a.cu_tokens, a.num_seqs, t0, lane);
+        const int32_t cb = a.cu_tokens[b], ce = a.cu_tokens[b + 1];
+        const bool one_seq = t0 + nt <= ce;
+        int32_t bj = b, rel = t0 + lane - cb;
+        if (!one_seq && lane < nt) {
+            int32_t lo = 0, hi = a.num_seqs - 1;
+            const int32_t tok = t0 + lane;
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (a.cu_tokens[mid] <= tok) lo = mid; else hi = mid - 1;
+            }
+            bj = lo;
+            rel = tok - a.cu_tokens[lo];
+        }
+        if (lane < 16) {
+            int64_t ph = -1;
+            int32_t slot = 0;
+            if (lane < nt) {
+                const int32_t pos = a.start_pos[bj] + rel;
+                const int32_t pg = pos >> 4;
+                const int32_t phys =
+                    (pos >= 0 && pg < a.max_pages) ? a.page_table[(int64_t)bj * a.max_pages + pg] : -1;
+                if ((uint32_t)phys < (uint32_t)a.num_pages) {
+                    ph = (int64_t)phys * a.hkv + h;
+                    slot = pos & 15;
+                } else {
+                    note_bad_id(a.bad_ids, kBadIdStore);
+                }
+            }
+            head_of[lane] = ph;
+            slot_of[lane] = slot;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = 4 * wave + r;
+        float kmax = 0.0f, vmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            kmax = fmaxf(kmax, fabsf(kx[r][e]));
+            vmax = fmaxf(vmax, fabsf(vx[r][e]));
+        }
+        kmax = wave_max(kmax);
+        vmax = wave_max(vmax);
+        const float ks = kmax / kMax;   // IEEE division, as the row kernel
+        const float vs = vmax / kMax;
+        uint8_t kc[EPL], vc[EPL];
+        encode<EPL, FP8>(kx[r], ks, kc);
+        encode<EPL, FP8>(vx[r], vs, vc);
+        if constexpr (EPL == 8) *reinterpret_cast<u32x2*>(vq + j * D + lane * EPL) = *reinterpret_cast<u32x2*>(vc);
+        else *reinterpret_cast<uint32_t*>(vq + j * D + lane * EPL) = *reinterpret_cast<uint32_t*>(vc);
+        const int64_t ph = head_of[j];
+        if (j < nt && ph >= 0) {
+            const int32_t slot = slot_of[j];
+            uint8_t* kdst = a.k_slab + (ph * kPage + slot) * D + lane * EPL;
+            if constexpr (EPL == 8) *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<u32x2*>(kc);
+            else *reinterpret_cast<uint32_t*>(kdst) = *reinterpret_cast<uint32_t*>(kc);
+            if (lane == 0) {
+                a.k_scale[ph * kPage + slot] = ks;
+                a.v_scale[ph * kPage + slot] = vs;
+            }
+        }
+    }
+    __syncthreads();
+    bool whole = nt == 16 && head_of[0] >= 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) whole = whole && head_of[j] == head_of[0] && slot_of[j] == j;
+#pragma unroll
+    for (int dd = 0; dd < D / 256; ++dd) {
+        const int d = t + 256 * dd;
+        uint8_t* vrow = a.v_slab + d * kPage;
+        if (whole) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)vq[(4 * e) * D + d] | ((uint32_t)vq[(4 * e + 1) * D + d] << 8) |
+                       ((uint32_t)vq[(4 * e + 2) * D + d] << 16) | ((uint32_t)vq[(4 * e + 3) * D + d] << 24);
+            *reinterpret_cast<u32x4*>(vrow + head_of[0] * kPage * D) = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+            for (int j = 0; j < nt; ++j)
+                if (head_of[j] >= 0) vrow[head_of[j] * kPage * D + slot_of[j]] = vq[j * D + d];
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void step_positions_kernel(const int32_t* kv_lens, int32_t B, int32_t* cu,
                                                                int32_t* start) {
     const int32_t b = blockIdx.x * 256 + threadIdx.x;
@@ -382,6 +498,17 @@ int launch_store(const StoreLaunch& s, void* stream) {
     } else if (s.kv_dtype == PAKV_KV_BF16) {
         if (s.head_dim == 256) launch(K, store_bf16_kernel<256>, grid, dim3(256), 0, st, a);
         else launch(K, store_bf16_kernel<512>, grid, dim3(256), 0, st, a);
+    } else if (s.total_tokens >= 4 * s.num_seqs) {
+        // 8-bit chunks: whole V pages of codes
+        const dim3 pgrid((s.total_tokens + 15) / 16, s.hkv);
+        const bool fp8 = s.kv_dtype == PAKV_KV_FP8_PTH;
+        if (s.head_dim == 256) {
+            if (fp8) launch(K, store_q8_pages_kernel<256, true>, pgrid, dim3(256), 0, st, a);
+            else launch(K, store_q8_pages_kernel<256, false>, pgrid, dim3(256), 0, st, a);
+        } else {
+            if (fp8) launch(K, store_q8_pages_kernel<512, true>, pgrid, dim3(256), 0, st, a);
+            else launch(K, store_q8_pages_kernel<512, false>, pgrid, dim3(256), 0, st, a);
+        }
     } else if (s.kv_dtype == PAKV_KV_FP8_PTH) {
         if (s.head_dim == 256) launch(K, store_q8_kernel<256, true>, grid, dim3(256), 0, st, a);
         else launch(K, store_q8_kernel<512, true>, grid, dim3(256), 0, st, a);
