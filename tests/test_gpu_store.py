@@ -198,3 +198,64 @@ def test_shared_layer_store_changes_nothing():
     for x, y in zip(before, after):
         assert torch.equal(x, y)
     assert set(sc.cache.slabs) == {0, 1}
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("case", ["whole_pages", "ragged", "one_token_each", "dropped"])
+@pytest.mark.parametrize("d,hkv", [(256, 1), (512, 2)])
+def test_store_q8_paths_bit_exact(fmt, case, d, hkv):
+    """8-bit chunks (four or more tokens per sequence on average) go through the
+    kernel that writes whole V pages (16-byte dim rows when 16 tokens fill a
+    page, single codes otherwise), fewer through the row kernel: codes and
+    scales equal the oracle's encoding of every row either way, rows without a
+    page are dropped, and unwritten slots keep their sentinel."""
+    from oracle import fp8_pth
+    need_gpu()
+    if case == "whole_pages":
+        caps, starts, counts = [64, 32, 96, 16], [0, 16, 32, 0], [64, 16, 48, 16]
+    elif case == "one_token_each":
+        caps = [1, 17, 33, 16, 5, 200, 31, 2]
+        starts, counts = [c - 1 for c in caps], [1] * 8
+    else:
+        caps, starts, counts = [40, 7, 100, 33, 19], [3, 0, 21, 32, 2], [37, 7, 79, 1, 17]
+    spec = LayerSpec("full", d, hkv, hkv, 0, kv_dtype=fmt)
+    sc = Scenario([spec], None, caps, seed=91 + d + len(case) + len(fmt))
+    table = sc.pool.page_table.copy()
+    if case == "dropped":
+        table[0, 1] = sc.pool.num_pages + 3           # outside the pool
+        table[2, 3] = -1                              # no page
+        sc.cache.set_page_table(table)
+    kc0, vc0 = [t.clone() for t in sc.cache.slabs[0][:2]]
+    total = sum(counts)
+    k = normal_bf16(sc.rng, (total, hkv, d))
+    v = normal_bf16(sc.rng, (total, hkv, d))
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    sc.cache.store(0, i32(cu), i32(starts), dev_bits(k), dev_bits(v))
+    torch.cuda.synchronize()
+    u8 = lambda t: t.cpu().numpy().view(np.uint8)
+    kc, vc = u8(sc.cache.slabs[0][0]), u8(sc.cache.slabs[0][1])
+    ksc, vsc = sc.cache.slabs[0][2].cpu().numpy(), sc.cache.slabs[0][3].cpu().numpy()
+    quant = fp8_pth.quantise_rows if fmt == "fp8" else quantise_rows
+    kq, kscale = quant(bf16_to_f32(k))
+    vq, vscale = quant(bf16_to_f32(v))
+    kq, vq = kq.view(np.uint8), vq.view(np.uint8)
+    written = np.zeros((sc.pool.num_pages, 16), dtype=bool)
+    stored = 0
+    for b in range(len(caps)):
+        for i in range(counts[b]):
+            pos, t = starts[b] + i, cu[b] + i
+            page = table[b, pos // 16]
+            if not (0 <= page < sc.pool.num_pages):
+                continue
+            written[page, pos % 16] = True
+            stored += 1
+            for h in range(hkv):
+                assert np.array_equal(kc[page, h, pos % 16, :], kq[t, h]), (b, i, h)
+                assert np.array_equal(vc[page, h, :, pos % 16], vq[t, h]), (b, i, h)
+                assert kscale[t, h].tobytes() == ksc[page, h, pos % 16].tobytes()
+                assert vscale[t, h].tobytes() == vsc[page, h, pos % 16].tobytes()
+    assert stored == total or case == "dropped"
+    assert case != "dropped" or 0 < stored < total
+    k0, v0 = u8(kc0), u8(vc0)
+    assert np.array_equal(kc.transpose(0, 2, 1, 3)[~written], k0.transpose(0, 2, 1, 3)[~written])
+    assert np.array_equal(vc.transpose(0, 3, 1, 2)[~written], v0.transpose(0, 3, 1, 2)[~written])
